@@ -1,0 +1,215 @@
+"""Python binding of libfa (exact tiled attention for MI355X).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libfa.so``.  PyTorch supplies device memory and the current
+stream.  If the library has not been built this module raises on first use;
+there is no fallback path.
+
+    o, lse = forward(q, k, v, scale, causal=False, blockmask=None)
+    dq, dk, dv = backward(q, k, v, o, do, lse, scale, causal=False, blockmask=None)
+
+Tensors are [B, H, N, d] bfloat16, contiguous, on one GPU; ``blockmask`` is
+a uint8 [nb, nb] tensor on the same GPU (nb = ceil(N / mask_block)).
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+import re
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libfa.so")
+HEADER = os.path.join(os.path.dirname(PKG_DIR), "include", "fa.h")
+
+FA_OK = 0
+FA_ERR_NULL = 1
+FA_ERR_SHAPE = 2
+FA_ERR_UNSUPPORTED = 3
+FA_ERR_WORKSPACE = 4
+FA_ERR_HIP = 5
+
+_lib = None
+
+_vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_SIGNATURES = {
+    "fa_fwd": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i, _vp, _vp, _vp]),
+    "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i]),
+    "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i,
+                    _vp, _vp, _vp, _vp, _sz, _vp]),
+    "fa_strerror": (ctypes.c_char_p, [_i]),
+}
+
+
+class LibfaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libfa.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(
+            f"libfa.so not found at {path}; build it with `python -m exact_io_aware_62_amd.build`")
+    lib = ctypes.CDLL(path)
+    for name, (res, args) in _SIGNATURES.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = lib
+    return lib
+
+
+def header_functions(path: str = HEADER) -> list[str]:
+    """Names of the functions include/fa.h declares."""
+    with open(path) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(fa_\w+)\s*\(", text, flags=re.M)
+
+
+def strerror(status: int) -> str:
+    return load_library().fa_strerror(int(status)).decode()
+
+
+def bwd_workspace_bytes(B: int, H: int, N: int, d: int) -> int:
+    return int(load_library().fa_bwd_workspace_bytes(B, H, N, d))
+
+
+# ---------------------------------------------------------------------------
+# torch-facing wrappers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch  # local: the C ABI itself needs no torch
+    return torch
+
+
+def _check(t, name, dtype, shape=None, device=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on a GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (BHND)")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+
+
+def _mask_args(blockmask, N, mask_block, device):
+    torch = _torch()
+    if blockmask is None:
+        return None, 0
+    nb = -(-N // mask_block)
+    _check(blockmask, "blockmask", torch.uint8, (nb, nb), device)
+    return blockmask.data_ptr(), mask_block
+
+
+def _stream_ptr(device):
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)
+
+
+def forward(q, k, v, scale: float | None = None, causal: bool = False, blockmask=None,
+            mask_block: int = 128, out=None, lse=None):
+    """O, LSE = attention forward.  Returns (o [B,H,N,d] bf16, lse [B,H,N] fp32)."""
+    torch = _torch()
+    _check(q, "q", torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    dev = q.device
+    _check(k, "k", torch.bfloat16, q.shape, dev)
+    _check(v, "v", torch.bfloat16, q.shape, dev)
+    scale = default_scale(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty_like(q)
+    else:
+        _check(out, "out", torch.bfloat16, q.shape, dev)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    else:
+        _check(lse, "lse", torch.float32, (B, H, N), dev)
+    bm_ptr, mb = _mask_args(blockmask, N, mask_block, dev)
+    rc = load_library().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, d, scale,
+                               int(bool(causal)), bm_ptr, mb, out.data_ptr(), lse.data_ptr(),
+                               _stream_ptr(dev))
+    if rc != FA_OK:
+        raise LibfaError(rc, "fa_fwd")
+    return out, lse
+
+
+def backward(q, k, v, o, do, lse, scale: float | None = None, causal: bool = False,
+             blockmask=None, mask_block: int = 128, workspace=None, dq=None, dk=None, dv=None):
+    """dQ, dK, dV of sum(dO * O).  Returns three [B,H,N,d] bf16 tensors."""
+    torch = _torch()
+    _check(q, "q", torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(t, name, torch.bfloat16, q.shape, dev)
+    _check(lse, "lse", torch.float32, (B, H, N), dev)
+    scale = default_scale(d) if scale is None else float(scale)
+    outs = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty_like(q)
+        else:
+            _check(t, name, torch.bfloat16, q.shape, dev)
+        outs.append(t)
+    nbytes = bwd_workspace_bytes(B, H, N, d) if d in (64, 128) else 0
+    if workspace is None:
+        workspace = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=dev)
+    bm_ptr, mb = _mask_args(blockmask, N, mask_block, dev)
+    rc = load_library().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                               do.data_ptr(), lse.data_ptr(), B, H, N, d, scale,
+                               int(bool(causal)), bm_ptr, mb, outs[0].data_ptr(),
+                               outs[1].data_ptr(), outs[2].data_ptr(), workspace.data_ptr(),
+                               workspace.numel() * workspace.element_size(), _stream_ptr(dev))
+    if rc != FA_OK:
+        raise LibfaError(rc, "fa_bwd")
+    return tuple(outs)
+
+
+class FlashAttention:
+    """torch.autograd.Function adapter over forward/backward (built lazily)."""
+
+    _fn = None
+
+    @classmethod
+    def apply(cls, q, k, v, scale=None, causal=False, blockmask=None, mask_block=128):
+        if cls._fn is None:
+            torch = _torch()
+
+            class _Fn(torch.autograd.Function):
+                @staticmethod
+                def forward(ctx, q, k, v, scale, causal, blockmask, mask_block):
+                    o, lse = forward(q, k, v, scale, causal, blockmask, mask_block)
+                    ctx.save_for_backward(q, k, v, o, lse)
+                    ctx.args = (scale, causal, blockmask, mask_block)
+                    return o
+
+                @staticmethod
+                def backward(ctx, do):
+                    q, k, v, o, lse = ctx.saved_tensors
+                    dq, dk, dv = backward(q, k, v, o, do.contiguous(), lse, *ctx.args)
+                    return dq, dk, dv, None, None, None, None
+
+            cls._fn = _Fn
+        return cls._fn.apply(q, k, v, scale, causal, blockmask, mask_block)

@@ -1,0 +1,129 @@
+// C entry points of libfa: argument validation and kernel dispatch.
+//
+// Every check runs before the first HIP call, so invalid arguments never
+// launch anything and can be exercised without a GPU.  See include/fa.h for
+// the contract of each call.
+
+#include "fa.h"
+
+#include <cmath>
+#include <cstdint>
+
+#include "fa_launch.hpp"
+
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr long long kMaxI32 = 2147483647LL;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shared validation of shapes, scalars and masks.  Sets *empty when there is
+// nothing to compute.
+int check_common(int B, int H, int N, int d, float scale, const uint8_t* blockmask,
+                 int mask_block, bool* empty) {
+  if (B < 0 || H < 0 || N < 0 || d < 0) return FA_ERR_SHAPE;
+  if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_UNSUPPORTED;
+  if (blockmask != nullptr && (mask_block <= 0 || mask_block % 128 != 0))
+    return FA_ERR_UNSUPPORTED;
+  if ((long long)N * d > kMaxI32) return FA_ERR_UNSUPPORTED;
+  const long long nqb = ((long long)N + 127) / 128;
+  if (nqb * B * H > kMaxI32) return FA_ERR_UNSUPPORTED;
+  *empty = (long long)B * H * N == 0;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "success";
+    case FA_ERR_NULL: return "libfa: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "libfa: negative dimension";
+    case FA_ERR_UNSUPPORTED:
+      return "libfa: unsupported arguments (need d in {64,128}, finite scale > 0, "
+             "mask_block a multiple of 128, 16-byte aligned tensors, sizes below 2^31)";
+    case FA_ERR_WORKSPACE: return "libfa: workspace missing or too small";
+    case FA_ERR_HIP: return "libfa: HIP runtime error at kernel launch";
+    default: return "libfa: unknown status";
+  }
+}
+
+int fa_fwd(const void* Q, const void* K, const void* V, int B, int H, int N, int d, float scale,
+           int causal, const uint8_t* blockmask, int mask_block, void* O, float* LSE,
+           hipStream_t stream) {
+  bool empty = false;
+  int rc = check_common(B, H, N, d, scale, blockmask, mask_block, &empty);
+  if (rc != FA_OK) return rc;
+  if (empty) return FA_OK;
+  if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
+      !aligned(LSE, 4))
+    return FA_ERR_UNSUPPORTED;
+
+  fa::FwdParams p;
+  p.Q = static_cast<const uint16_t*>(Q);
+  p.K = static_cast<const uint16_t*>(K);
+  p.V = static_cast<const uint16_t*>(V);
+  p.O = static_cast<uint16_t*>(O);
+  p.LSE = LSE;
+  p.blockmask = blockmask;
+  p.BH = B * H;
+  p.N = N;
+  p.nqb = (N + 127) / 128;
+  p.mask_block = blockmask ? mask_block : 128;
+  p.nbm = (N + p.mask_block - 1) / p.mask_block;
+  p.scale_log2 = scale * kLog2e;
+  hipError_t e = fa::launch_fwd(p, d, causal != 0, blockmask != nullptr, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
+  if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128)) return 0;
+  return (size_t)4 * (size_t)B * (size_t)H * (size_t)N;
+}
+
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+           const float* LSE, int B, int H, int N, int d, float scale, int causal,
+           const uint8_t* blockmask, int mask_block, void* dQ, void* dK, void* dV,
+           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  bool empty = false;
+  int rc = check_common(B, H, N, d, scale, blockmask, mask_block, &empty);
+  if (rc != FA_OK) return rc;
+  if (empty) return FA_OK;
+  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL;
+  if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d))
+    return FA_ERR_WORKSPACE;
+  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
+      !aligned(dO, 16) || !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16) ||
+      !aligned(LSE, 4) || !aligned(workspace, 4))
+    return FA_ERR_UNSUPPORTED;
+
+  fa::BwdParams p;
+  p.Q = static_cast<const uint16_t*>(Q);
+  p.K = static_cast<const uint16_t*>(K);
+  p.V = static_cast<const uint16_t*>(V);
+  p.O = static_cast<const uint16_t*>(O);
+  p.dO = static_cast<const uint16_t*>(dO);
+  p.LSE = LSE;
+  p.Dsum = static_cast<float*>(workspace);
+  p.dQ = static_cast<uint16_t*>(dQ);
+  p.dK = static_cast<uint16_t*>(dK);
+  p.dV = static_cast<uint16_t*>(dV);
+  p.blockmask = blockmask;
+  p.BH = B * H;
+  p.N = N;
+  p.nqb = (N + 127) / 128;
+  p.nkb = (N + 127) / 128;
+  p.mask_block = blockmask ? mask_block : 128;
+  p.nbm = (N + p.mask_block - 1) / p.mask_block;
+  p.scale = scale;
+  p.scale_log2 = scale * kLog2e;
+  hipError_t e = fa::launch_bwd(p, d, causal != 0, blockmask != nullptr, stream);
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // extern "C"

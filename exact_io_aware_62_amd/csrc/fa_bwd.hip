@@ -1,0 +1,422 @@
+// Backward kernels: recompute S and P from Q, K and the saved LSE and form
+// dQ, dK, dV (FlashAttention-NeurIPS22 digest, "核心方法", Backward
+// recomputation: only O and the softmax normalisers are kept from the
+// forward, S and P are rebuilt on chip).
+//
+// With P = softmax(S), S = scale * Q K^T (+ mask), and L = sum(dO * O):
+//   dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij = sum_k dO_ik O_ik,
+//   dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
+//
+// Three launches, all deterministic (no atomics; FlashAttention-2 wiki,
+// "性能与效率": exact and deterministic):
+//   1. dsum_kernel   D_i from the O actually handed in (bf16) and dO;
+//   2. dkdv_kernel   one workgroup per 128 keys of one head, looping over
+//                    query tiles: dV and dK accumulate in registers and are
+//                    written once;
+//   3. dq_kernel     one workgroup per 128 query rows, looping over key
+//                    tiles: dQ accumulates in registers and is written once.
+// Both main kernels split the sequence over workgroups the way the forward
+// does (FlashAttention-2 wiki, "技术架构与工作原理", item 2).
+
+#include "fa_common.hpp"
+#include "fa_launch.hpp"
+
+namespace fa {
+
+// log2-domain LSE with the empty-row convention folded in: an empty row
+// (LSE = -inf) maps to +inf so that exp2(s - lse2) is exactly 0.
+__device__ __forceinline__ float lse_to_log2(float lse) {
+  return lse == -INFINITY ? INFINITY : lse * kLog2e;
+}
+
+// ---------------------------------------------------------------------------
+// 1. D_i = sum_k dO_ik * O_ik  (fp32 accumulation, fixed order)
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void dsum_kernel(BwdParams p, long long rows) {
+  constexpr int LPR = D / 8;                 // lanes per row, 8 elements each
+  constexpr int RPB = 256 / LPR;             // rows per workgroup
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / LPR;
+  const int part = threadIdx.x % LPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const u32x4 o = ldg16(p.O + row * D + part * 8);
+    const u32x4 g = ldg16(p.dO + row * D + part * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float o0 = __uint_as_float(o[i] << 16), o1 = __uint_as_float(o[i] & 0xffff0000u);
+      const float g0 = __uint_as_float(g[i] << 16), g1 = __uint_as_float(g[i] & 0xffff0000u);
+      acc = __builtin_fmaf(o0, g0, acc);
+      acc = __builtin_fmaf(o1, g1, acc);
+    }
+  }
+#pragma unroll
+  for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (row < rows && part == 0) p.Dsum[row] = acc;
+}
+
+// ---------------------------------------------------------------------------
+// 2. dK, dV.  Workgroup = 4 wavefronts = 128 keys; wavefront w owns keys
+//    kw .. kw+31 and keeps K and V rows for them in registers.  Query tiles
+//    of 64 rows stream through LDS (double-buffered) in two layouts: natural
+//    (for S = Q K^T and dP = dO V^T, contraction over d) and transposed (for
+//    dV^T += dO^T P and dK^T += Q^T dS, contraction over queries).
+//    Scores are formed as S (queries x keys) so each lane owns one key and
+//    the P / dS fragments feed the dV / dK products as B operands directly.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
+  constexpr int BKB = 128, BQ = 64, NT = 256;
+  constexpr int NDB = D / 32, NKK = D / 16, NQB = BQ / 32;
+  using NStage = NaturalStage<BQ, D, NT>;
+  using TStage = TransposedStage<BQ, D, NT>;
+  constexpr int NS = NStage::kStride, TS = TStage::kStride;
+  // per buffer: Q, dO natural; Q, dO transposed; lse2[BQ]; D[BQ]
+  constexpr int OFF_QN = 0;
+  constexpr int OFF_ON = OFF_QN + NStage::kElems;
+  constexpr int OFF_QT = OFF_ON + NStage::kElems;
+  constexpr int OFF_OT = OFF_QT + TStage::kElems;
+  constexpr int OFF_ROW = OFF_OT + TStage::kElems;   // 2 * BQ floats
+  constexpr int BUF = OFF_ROW + 2 * BQ * 2;          // in uint16 units
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, r = lane & 31, g = lane >> 5;
+  const BlockCoord bc = block_coord(p.BH);
+  const int kb = bc.blk;
+  const int N = p.N;
+  const size_t head = (size_t)bc.bh * N * D;
+  const uint16_t* __restrict__ Qh = p.Q + head;
+  const uint16_t* __restrict__ dOh = p.dO + head;
+  const float* __restrict__ lseh = p.LSE + (size_t)bc.bh * N;
+  const float* __restrict__ Dh = p.Dsum + (size_t)bc.bh * N;
+
+  const int kw = kb * BKB + w * 32;   // first key of this wavefront
+  const int key = kw + r;             // this lane's key
+  bf16x8 kf[NKK], vf[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const size_t off = (size_t)key * D + kk * 16 + g * 8;
+    kf[kk] = as_bf16x8(key < N ? ldg16(p.K + head + off) : zero_u32x4());
+    vf[kk] = as_bf16x8(key < N ? ldg16(p.V + head + off) : zero_u32x4());
+  }
+
+  // query tiles: causal => only rows >= first key of the block
+  const int nqt = (N + BQ - 1) / BQ;
+  const int t_begin = CAUSAL ? (kb * BKB) / BQ : 0;
+  const int mcol = SPARSE ? (kb * BKB) / p.mask_block : 0;
+  auto active = [&](int t) -> bool {
+    if (!SPARSE) return true;
+    return p.blockmask[(size_t)((t * BQ) / p.mask_block) * p.nbm + mcol] != 0;
+  };
+  auto next_tile = [&](int t) -> int {
+    while (t < nqt && !active(t)) ++t;
+    return t;
+  };
+
+  f32x16 dv[NDB], dk[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    dv[db] = zero16();
+    dk[db] = zero16();
+  }
+  const float c = p.scale_log2;
+
+  NStage qn, on;
+  TStage qt, ot;
+  float rowv = 0.f;   // thread tid < 2*BQ stages one lse2 / D value
+  auto load_tile = [&](int t) {
+    qn.load(Qh, t * BQ, N, tid);
+    on.load(dOh, t * BQ, N, tid);
+    qt.load(Qh, t * BQ, N, tid);
+    ot.load(dOh, t * BQ, N, tid);
+    if (tid < 2 * BQ) {
+      const int q = t * BQ + (tid % BQ);
+      if (tid < BQ)
+        rowv = q < N ? lse_to_log2(lseh[q]) : INFINITY;
+      else
+        rowv = q < N ? Dh[q] : 0.f;
+    }
+  };
+  auto store_tile = [&](uint16_t* b) {
+    qn.store(b + OFF_QN, tid);
+    on.store(b + OFF_ON, tid);
+    qt.store(b + OFF_QT, tid);
+    ot.store(b + OFF_OT, tid);
+    if (tid < 2 * BQ) reinterpret_cast<float*>(b + OFF_ROW)[tid] = rowv;
+  };
+
+  int t = next_tile(t_begin);
+  if (t < nqt) {
+    load_tile(t);
+    store_tile(lds);
+  }
+  int buf = 0;
+  while (t < nqt) {
+    __syncthreads();
+    const int tn = next_tile(t + 1);
+    if (tn < nqt) load_tile(tn);
+    const uint16_t* b = lds + buf * BUF;
+    const float* lse2 = reinterpret_cast<const float*>(b + OFF_ROW);
+    const float* dsum = lse2 + BQ;
+    const int q0 = t * BQ;
+    const bool live = !CAUSAL || q0 + BQ - 1 >= kw;
+    if (live) {
+      // S = Q K^T and dP = dO V^T for NQB blocks of 32 queries
+      f32x16 s[NQB], dp[NQB];
+#pragma unroll
+      for (int qb2 = 0; qb2 < NQB; ++qb2) {
+        s[qb2] = zero16();
+        dp[qb2] = zero16();
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          s[qb2] = mfma32x32x16(lds_row8(b + OFF_QN, NS, qb2 * 32 + r, kk * 16 + g * 8), kf[kk],
+                                s[qb2]);
+          dp[qb2] = mfma32x32x16(lds_row8(b + OFF_ON, NS, qb2 * 32 + r, kk * 16 + g * 8), vf[kk],
+                                 dp[qb2]);
+        }
+      }
+      const bool need_mask = (CAUSAL && q0 < kw + 31) || (q0 + BQ > N) || (kw + 32 > N);
+      // P = exp2(S * c - lse2[q]);  dS = P * (dP - D[q])
+#pragma unroll
+      for (int qb2 = 0; qb2 < NQB; ++qb2)
+#pragma unroll
+        for (int i4 = 0; i4 < 4; ++i4) {
+          const int ql = qb2 * 32 + i4 * 8 + g * 4;   // local query of register i4*4
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + ql);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dsum + ql);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int i = i4 * 4 + j;
+            float sv = s[qb2][i];
+            if (need_mask) {
+              const int q = q0 + ql + j;
+              if ((CAUSAL && key > q) || q >= N || key >= N) sv = -INFINITY;
+            }
+            const float pv = exp2_fast(__builtin_fmaf(sv, c, -l4[j]));
+            s[qb2][i] = pv;
+            dp[qb2][i] = pv * (dp[qb2][i] - d4[j]);
+          }
+        }
+      // dV^T += dO^T P ;  dK^T += Q^T dS   (contraction over queries)
+#pragma unroll
+      for (int qb2 = 0; qb2 < NQB; ++qb2)
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2) {
+          const int e = 8 * ks2;
+          const bf16x8 pb = pack_bf16x8(s[qb2][e + 0], s[qb2][e + 1], s[qb2][e + 2], s[qb2][e + 3],
+                                        s[qb2][e + 4], s[qb2][e + 5], s[qb2][e + 6], s[qb2][e + 7]);
+          const bf16x8 sb =
+              pack_bf16x8(dp[qb2][e + 0], dp[qb2][e + 1], dp[qb2][e + 2], dp[qb2][e + 3],
+                          dp[qb2][e + 4], dp[qb2][e + 5], dp[qb2][e + 6], dp[qb2][e + 7]);
+          const int c0 = qb2 * 32 + 16 * ks2 + g * 4;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db) {
+            dv[db] = mfma32x32x16(lds_tr8(b + OFF_OT, TS, db * 32 + r, c0, c0 + 8), pb, dv[db]);
+            dk[db] = mfma32x32x16(lds_tr8(b + OFF_QT, TS, db * 32 + r, c0, c0 + 8), sb, dk[db]);
+          }
+        }
+    }
+    if (tn < nqt) store_tile(lds + (buf ^ 1) * BUF);
+    buf ^= 1;
+    t = tn;
+  }
+
+  // epilogue: lane owns key `key`; register i of block db is column
+  // db*32 + (i/4)*8 + g*4 + i%4
+  if (key < N) {
+    uint16_t* dKh = p.dK + head + (size_t)key * D;
+    uint16_t* dVh = p.dV + head + (size_t)key * D;
+    const float sc = p.scale;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd) {
+        const int col = db * 32 + qd * 8 + g * 4;
+        *reinterpret_cast<u32x2*>(dVh + col) =
+            pack_bf16x4(dv[db][qd * 4 + 0], dv[db][qd * 4 + 1], dv[db][qd * 4 + 2],
+                        dv[db][qd * 4 + 3]);
+        *reinterpret_cast<u32x2*>(dKh + col) =
+            pack_bf16x4(dk[db][qd * 4 + 0] * sc, dk[db][qd * 4 + 1] * sc, dk[db][qd * 4 + 2] * sc,
+                        dk[db][qd * 4 + 3] * sc);
+      }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 3. dQ.  Workgroup = 4 wavefronts = 128 query rows (32 per wavefront, held
+//    in registers with their dO rows).  Key tiles of 64 rows stream through
+//    LDS: K natural (S^T = K Q^T), V natural (dP^T = V dO^T) and K transposed
+//    (dQ^T += K^T dS^T).  Same transposed-score arrangement as the forward:
+//    each lane owns one query row, so LSE and D are per-lane scalars.
+// ---------------------------------------------------------------------------
+template <int D, bool CAUSAL, bool SPARSE>
+__global__ __launch_bounds__(256, 1) void dq_kernel(BwdParams p) {
+  constexpr int BQ = 128, BK = 64, NT = 256;
+  constexpr int NDB = D / 32, NKK = D / 16;
+  using NStage = NaturalStage<BK, D, NT>;
+  using TStage = TransposedStage<BK, D, NT>;
+  constexpr int NS = NStage::kStride, TS = TStage::kStride;
+  constexpr int OFF_KN = 0;
+  constexpr int OFF_VN = OFF_KN + NStage::kElems;
+  constexpr int OFF_KT = OFF_VN + NStage::kElems;
+  constexpr int BUF = OFF_KT + TStage::kElems;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BUF];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, w = tid >> 6, r = lane & 31, g = lane >> 5;
+  const BlockCoord bc = block_coord(p.BH);
+  const int qb = CAUSAL ? (p.nqb - 1 - bc.blk) : bc.blk;
+  const int N = p.N;
+  const size_t head = (size_t)bc.bh * N * D;
+  const uint16_t* __restrict__ Kh = p.K + head;
+  const uint16_t* __restrict__ Vh = p.V + head;
+
+  const int q0w = qb * BQ + w * 32;
+  const int qrow = q0w + r;
+  bf16x8 qf[NKK], of[NKK];
+#pragma unroll
+  for (int kk = 0; kk < NKK; ++kk) {
+    const size_t off = (size_t)qrow * D + kk * 16 + g * 8;
+    qf[kk] = as_bf16x8(qrow < N ? ldg16(p.Q + head + off) : zero_u32x4());
+    of[kk] = as_bf16x8(qrow < N ? ldg16(p.dO + head + off) : zero_u32x4());
+  }
+  const float lse2 = qrow < N ? lse_to_log2(p.LSE[(size_t)bc.bh * N + qrow]) : INFINITY;
+  const float dsum = qrow < N ? p.Dsum[(size_t)bc.bh * N + qrow] : 0.f;
+
+  const int kend = CAUSAL ? min(N, (qb + 1) * BQ) : N;
+  const int ntiles = (kend + BK - 1) / BK;
+  const int mrow = SPARSE ? (qb * BQ) / p.mask_block : 0;
+  auto active = [&](int t) -> bool {
+    if (!SPARSE) return true;
+    return p.blockmask[(size_t)mrow * p.nbm + (t * BK) / p.mask_block] != 0;
+  };
+  auto next_tile = [&](int t) -> int {
+    while (t < ntiles && !active(t)) ++t;
+    return t;
+  };
+
+  f32x16 dq[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dq[db] = zero16();
+  const float c = p.scale_log2;
+
+  NStage kn, vn;
+  TStage kt;
+  int t = next_tile(0);
+  if (t < ntiles) {
+    kn.load(Kh, t * BK, N, tid);
+    vn.load(Vh, t * BK, N, tid);
+    kt.load(Kh, t * BK, N, tid);
+    kn.store(lds + OFF_KN, tid);
+    vn.store(lds + OFF_VN, tid);
+    kt.store(lds + OFF_KT, tid);
+  }
+  int buf = 0;
+  while (t < ntiles) {
+    __syncthreads();
+    const int tn = next_tile(t + 1);
+    if (tn < ntiles) {
+      kn.load(Kh, tn * BK, N, tid);
+      vn.load(Vh, tn * BK, N, tid);
+      kt.load(Kh, tn * BK, N, tid);
+    }
+    const uint16_t* b = lds + buf * BUF;
+    const int k0 = t * BK;
+    const bool live = !CAUSAL || k0 <= q0w + 31;
+    if (live) {
+      f32x16 s[2], dp[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = zero16();
+        dp[kb] = zero16();
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk) {
+          s[kb] = mfma32x32x16(lds_row8(b + OFF_KN, NS, kb * 32 + r, kk * 16 + g * 8), qf[kk],
+                               s[kb]);
+          dp[kb] = mfma32x32x16(lds_row8(b + OFF_VN, NS, kb * 32 + r, kk * 16 + g * 8), of[kk],
+                                dp[kb]);
+        }
+      }
+      const bool need_mask = (CAUSAL && k0 + BK - 1 > q0w) || (k0 + BK > N);
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          float sv = s[kb][i];
+          if (need_mask) {
+            const int key = k0 + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+            if (key >= N || (CAUSAL && key > qrow)) sv = -INFINITY;
+          }
+          const float pv = exp2_fast(__builtin_fmaf(sv, c, -lse2));
+          dp[kb][i] = pv * (dp[kb][i] - dsum);
+        }
+      // dQ^T += K^T dS^T
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int ks2 = 0; ks2 < 2; ++ks2) {
+          const int e = 8 * ks2;
+          const bf16x8 sb =
+              pack_bf16x8(dp[kb][e + 0], dp[kb][e + 1], dp[kb][e + 2], dp[kb][e + 3],
+                          dp[kb][e + 4], dp[kb][e + 5], dp[kb][e + 6], dp[kb][e + 7]);
+          const int c0 = kb * 32 + 16 * ks2 + g * 4;
+#pragma unroll
+          for (int db = 0; db < NDB; ++db)
+            dq[db] = mfma32x32x16(lds_tr8(b + OFF_KT, TS, db * 32 + r, c0, c0 + 8), sb, dq[db]);
+        }
+    }
+    if (tn < ntiles) {
+      uint16_t* nb = lds + (buf ^ 1) * BUF;
+      kn.store(nb + OFF_KN, tid);
+      vn.store(nb + OFF_VN, tid);
+      kt.store(nb + OFF_KT, tid);
+    }
+    buf ^= 1;
+    t = tn;
+  }
+
+  if (qrow < N) {
+    uint16_t* dQh = p.dQ + head + (size_t)qrow * D;
+    const float sc = p.scale;
+#pragma unroll
+    for (int db = 0; db < NDB; ++db)
+#pragma unroll
+      for (int qd = 0; qd < 4; ++qd)
+        *reinterpret_cast<u32x2*>(dQh + db * 32 + qd * 8 + g * 4) =
+            pack_bf16x4(dq[db][qd * 4 + 0] * sc, dq[db][qd * 4 + 1] * sc,
+                        dq[db][qd * 4 + 2] * sc, dq[db][qd * 4 + 3] * sc);
+  }
+}
+
+template <int D, bool CAUSAL, bool SPARSE>
+static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
+  const long long rows = (long long)p.BH * p.N;
+  constexpr int RPB = 256 / (D / 8);
+  hipLaunchKernelGGL((dsum_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                     stream, p, rows);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, SPARSE>), dim3((unsigned)((long long)p.nkb * p.BH)),
+                     dim3(256), 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((dq_kernel<D, CAUSAL, SPARSE>), dim3((unsigned)((long long)p.nqb * p.BH)),
+                     dim3(256), 0, stream, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd(const BwdParams& p, int d, bool causal, bool sparse, hipStream_t stream) {
+  if (d == 64) {
+    if (causal) return sparse ? launch_bwd_t<64, true, true>(p, stream)
+                              : launch_bwd_t<64, true, false>(p, stream);
+    return sparse ? launch_bwd_t<64, false, true>(p, stream)
+                  : launch_bwd_t<64, false, false>(p, stream);
+  }
+  if (causal) return sparse ? launch_bwd_t<128, true, true>(p, stream)
+                            : launch_bwd_t<128, true, false>(p, stream);
+  return sparse ? launch_bwd_t<128, false, true>(p, stream)
+                : launch_bwd_t<128, false, false>(p, stream);
+}
+
+}  // namespace fa

@@ -1,0 +1,138 @@
+/*
+ * libfa — exact tiled attention (FlashAttention-2 forward and recomputation
+ * backward) for AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (per batch b and head h, rows q_i, k_j, v_j of Q, K, V):
+ *
+ *   S_ij = scale * <q_i, k_j>, then S_ij = -inf where the key is masked;
+ *   P    = row-wise softmax(S);   O = P V;   LSE_i = ln sum_j exp(S_ij).
+ *
+ * This is plain softmax attention, computed exactly (FlashAttention-2 wiki
+ * pages, opening paragraph: same result as standard attention, no loss of
+ * precision) but in one fused pass that keeps the N x N score matrix on chip
+ * (FlashAttention-NeurIPS22 digest, section "核心方法": tiling with an online
+ * softmax, kernel fusion of matmul + mask + softmax + matmul).  The forward
+ * saves only O and one softmax statistic per row, LSE; the backward
+ * recomputes S and P from Q, K and LSE instead of reading them from memory
+ * (same section, "Backward recomputation").
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Tensors are BHND: element (b, h, n, k) of a [B, H, N, d] tensor sits at
+ *   ((b * H + h) * N + n) * d + k, densely packed, no strides.
+ * - Q, K, V, O, dO, dQ, dK, dV hold IEEE bfloat16 bit patterns (uint16).
+ *   LSE and the workspace are float32.  All tensor pointers are DEVICE
+ *   pointers owned by the caller; the library never allocates or frees
+ *   memory and keeps no pointer after a call returns.
+ * - Masks.  causal != 0 masks key j for query i when j > i.  blockmask, if
+ *   not NULL, is a DEVICE pointer to nb x nb uint8 values (nb =
+ *   ceil(N / mask_block)), row-major, shared by every batch and head; key j
+ *   is masked for query i when blockmask[(i / mask_block) * nb +
+ *   j / mask_block] == 0 (block-sparse attention, digest section "核心方法",
+ *   Block-sparse 扩展: zero blocks are skipped).  Both masks may be combined.
+ * - A query row whose keys are all masked gets O = 0 and LSE = -inf, and
+ *   contributes nothing to dK or dV; its dQ row is 0.
+ * - Outputs are rounded to bfloat16 with round-to-nearest-even.
+ * - Work is enqueued on `stream` (NULL = the null stream) and the call
+ *   returns without synchronising.  Results are bitwise reproducible from
+ *   run to run: no atomics are used anywhere (FlashAttention-2 wiki,
+ *   "性能与效率": the algorithm is exact and deterministic).
+ * - Outputs must not overlap inputs or each other.
+ *
+ * Supported domain (anything else returns FA_ERR_UNSUPPORTED):
+ *   d in {64, 128}; N >= 0 (any length; a partial last tile is masked);
+ *   scale finite and > 0; mask_block a positive multiple of 128 when
+ *   blockmask != NULL (ignored otherwise); N * d < 2^31 and
+ *   ceil(N / 128) * B * H < 2^31.
+ *   B, H or N equal to 0 is a valid empty problem: nothing is launched.
+ *
+ * Errors.  Every argument check happens before any HIP call, and on error
+ * nothing is launched.  A launch failure is reported as FA_ERR_HIP (from
+ * hipGetLastError).  No C++ exception crosses this interface.
+ */
+#ifndef LIBFA_FA_H
+#define LIBFA_FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL                         */
+  FA_ERR_SHAPE = 2,       /* a negative dimension                               */
+  FA_ERR_UNSUPPORTED = 3, /* outside the supported domain listed above          */
+  FA_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than fa_bwd_workspace_bytes */
+  FA_ERR_HIP = 5          /* the HIP runtime reported an error at launch        */
+} fa_status;
+
+/*
+ * Forward pass: O = softmax(scale * Q K^T + mask) V and LSE.
+ *
+ * The running row maximum and row sum of the online softmax (digest section
+ * "核心方法", Tiling 与 online softmax) are merged tile by tile; the division
+ * by the row sum is applied once at the end (FlashAttention-2 wiki,
+ * "技术架构与工作原理", item 1: fewer non-matmul operations).
+ *
+ *   Q, K, V    [B, H, N, d] bf16, read only.
+ *   O          [B, H, N, d] bf16, written.
+ *   LSE        [B, H, N] float32, written: natural-log log-sum-exp of the
+ *              scaled, masked scores of each row (-inf for an empty row).
+ *   scale      multiplies Q K^T before masking.
+ *   blockmask  NULL (no block mask) or device uint8 [nb, nb], see above.
+ *
+ * Returns FA_OK, or FA_ERR_NULL / FA_ERR_SHAPE / FA_ERR_UNSUPPORTED /
+ * FA_ERR_HIP.
+ */
+int fa_fwd(const void* Q, const void* K, const void* V,
+           int B, int H, int N, int d, float scale, int causal,
+           const uint8_t* blockmask, int mask_block,
+           void* O, float* LSE, hipStream_t stream);
+
+/*
+ * Bytes of device workspace fa_bwd needs: one float32 per query row for
+ * D_i = sum_k dO_ik * O_ik, i.e. 4 * B * H * N (0 for invalid or empty
+ * arguments).
+ */
+size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
+
+/*
+ * Backward pass: gradients of L = sum(dO * O) with respect to Q, K and V,
+ * recomputing S and P from Q, K and the saved LSE (digest section "核心方法",
+ * Backward recomputation).  Three stream-ordered launches:
+ *   1. D_i = sum_k dO_ik * O_ik  (into the workspace);
+ *   2. per block of keys: dV = P^T dO, dP = dO V^T, dS = P * (dP - D),
+ *      dK = scale * dS^T Q;
+ *   3. per block of queries: dQ = scale * dS K, recomputing dS; dQ is
+ *      written once, so no atomics are needed.
+ *
+ *   Q, K, V, O, dO   [B, H, N, d] bf16, read only.  O and LSE must be the
+ *                    outputs of fa_fwd for the same Q, K, V, scale and
+ *                    masks.
+ *   LSE              [B, H, N] float32, read only.
+ *   dQ, dK, dV       [B, H, N, d] bf16, written.
+ *   workspace        device memory of at least fa_bwd_workspace_bytes(),
+ *                    4-byte aligned; contents on entry are ignored.
+ *
+ * Returns FA_OK, or FA_ERR_NULL / FA_ERR_SHAPE / FA_ERR_UNSUPPORTED /
+ * FA_ERR_WORKSPACE / FA_ERR_HIP.
+ */
+int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
+           const void* dO, const float* LSE,
+           int B, int H, int N, int d, float scale, int causal,
+           const uint8_t* blockmask, int mask_block,
+           void* dQ, void* dK, void* dV,
+           void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Static, human-readable text for a status code (never NULL). */
+const char* fa_strerror(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBFA_FA_H */

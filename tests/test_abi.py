@@ -1,0 +1,111 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fa.h declares, and rejects every invalid argument before any HIP call
+(a HIP call on a machine without a GPU would surface as FA_ERR_HIP instead of
+the status asserted here)."""
+
+import ctypes
+import math
+import os
+
+import pytest
+
+import exact_io_aware_62_amd as fa
+
+FAKE = 0x10000  # never dereferenced: validation fails before any use
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(fa.LIB_PATH):
+        pytest.fail("libfa.so is not built (run __graft_entry__.build())")
+    return fa.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = fa.header_functions()
+    assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_strerror"}
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_strerror(lib):
+    for code in range(6):
+        s = fa.strerror(code)
+        assert s and isinstance(s, str)
+    assert "unknown" in fa.strerror(99)
+
+
+def fwd(lib, q=FAKE, k=FAKE, v=FAKE, B=1, H=1, N=128, d=64, scale=0.125, causal=0,
+        bm=None, mb=0, o=FAKE, lse=FAKE):
+    return lib.fa_fwd(q, k, v, B, H, N, d, scale, causal, bm, mb, o, lse, None)
+
+
+def bwd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, B=1, H=1, N=128, d=64,
+        scale=0.125, causal=0, bm=None, mb=0, dq=FAKE, dk=FAKE, dv=FAKE, ws=FAKE,
+        wsb=1 << 20):
+    return lib.fa_bwd(q, k, v, o, do, lse, B, H, N, d, scale, causal, bm, mb, dq, dk, dv, ws,
+                      wsb, None)
+
+
+@pytest.mark.parametrize("call", [fwd, bwd])
+def test_shape_and_domain_errors(lib, call):
+    assert call(lib, B=-1) == fa.FA_ERR_SHAPE
+    assert call(lib, H=-2) == fa.FA_ERR_SHAPE
+    assert call(lib, N=-1) == fa.FA_ERR_SHAPE
+    assert call(lib, d=-64) == fa.FA_ERR_SHAPE
+    for d in (0, 32, 96, 256):
+        assert call(lib, d=d) == fa.FA_ERR_UNSUPPORTED
+    for s in (float("nan"), float("inf"), -float("inf"), 0.0, -0.5):
+        assert call(lib, scale=s) == fa.FA_ERR_UNSUPPORTED
+    for mb in (0, -128, 64, 192):
+        assert call(lib, bm=FAKE, mb=mb) == fa.FA_ERR_UNSUPPORTED
+    # N * d beyond 2^31
+    assert call(lib, N=(1 << 31) // 64, d=64) == fa.FA_ERR_UNSUPPORTED
+    # too many workgroups
+    assert call(lib, B=1 << 16, H=1 << 10, N=128 * 64) == fa.FA_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("call", [fwd, bwd])
+def test_empty_problems_are_no_ops(lib, call):
+    # nothing to compute: OK even with NULL pointers
+    kw = dict(q=None, k=None, v=None, o=None, lse=None)
+    if call is bwd:
+        kw.update(do=None, dq=None, dk=None, dv=None, ws=None, wsb=0)
+    for dims in (dict(B=0), dict(H=0), dict(N=0)):
+        assert call(lib, **kw, **dims) == fa.FA_OK
+
+
+def test_null_pointers_fwd(lib):
+    for name in ("q", "k", "v", "o", "lse"):
+        assert fwd(lib, **{name: None}) == fa.FA_ERR_NULL, name
+
+
+def test_null_pointers_bwd(lib):
+    for name in ("q", "k", "v", "o", "do", "lse", "dq", "dk", "dv"):
+        assert bwd(lib, **{name: None}) == fa.FA_ERR_NULL, name
+
+
+def test_workspace_checks(lib):
+    need = lib.fa_bwd_workspace_bytes(2, 3, 200, 64)
+    assert need == 4 * 2 * 3 * 200
+    assert lib.fa_bwd_workspace_bytes(2, 3, 200, 96) == 0
+    assert lib.fa_bwd_workspace_bytes(-1, 3, 200, 64) == 0
+    assert bwd(lib, B=2, H=3, N=200, ws=None, wsb=need) == fa.FA_ERR_WORKSPACE
+    assert bwd(lib, B=2, H=3, N=200, ws=FAKE, wsb=need - 1) == fa.FA_ERR_WORKSPACE
+
+
+def test_alignment_checks(lib):
+    assert fwd(lib, q=FAKE + 2) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(lib, o=FAKE + 8) == fa.FA_ERR_UNSUPPORTED
+    assert fwd(lib, lse=FAKE + 2) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(lib, dk=FAKE + 4) == fa.FA_ERR_UNSUPPORTED
+    assert bwd(lib, ws=FAKE + 1) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_python_binding_rejects_bad_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 1, 8, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):      # CPU tensors are refused before any call
+        fa.forward(q, q, q)
+    with pytest.raises(TypeError):
+        fa.forward(q.float(), q, q)
