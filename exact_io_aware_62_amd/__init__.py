@@ -38,6 +38,11 @@ _SIGNATURES = {
     "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i,
                     _vp, _vp, _vp, _vp, _sz, _vp]),
+    "fa_bwd_dsum": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _vp]),
+    "fa_bwd_dkdv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i,
+                         _vp, _vp, _vp]),
+    "fa_bwd_dq": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i,
+                       _vp, _vp]),
     "fa_strerror": (ctypes.c_char_p, [_i]),
 }
 
@@ -185,6 +190,74 @@ def backward(q, k, v, o, do, lse, scale: float | None = None, causal: bool = Fal
     if rc != FA_OK:
         raise LibfaError(rc, "fa_bwd")
     return tuple(outs)
+
+
+def bwd_dsum(o, do, dsum=None):
+    """Stage 1 of the backward: D = rowsum(dO * O) as float32 [B, H, N]."""
+    torch = _torch()
+    _check(o, "o", torch.bfloat16)
+    B, H, N, d = o.shape
+    _check(do, "do", torch.bfloat16, o.shape, o.device)
+    if dsum is None:
+        dsum = torch.empty((B, H, N), dtype=torch.float32, device=o.device)
+    else:
+        _check(dsum, "dsum", torch.float32, (B, H, N), o.device)
+    rc = load_library().fa_bwd_dsum(o.data_ptr(), do.data_ptr(), B, H, N, d, dsum.data_ptr(),
+                                    _stream_ptr(o.device))
+    if rc != FA_OK:
+        raise LibfaError(rc, "fa_bwd_dsum")
+    return dsum
+
+
+def _stage_inputs(q, k, v, do, lse, dsum):
+    torch = _torch()
+    _check(q, "q", torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    for name, t in (("k", k), ("v", v), ("do", do)):
+        _check(t, name, torch.bfloat16, q.shape, q.device)
+    B, H, N, d = q.shape
+    _check(lse, "lse", torch.float32, (B, H, N), q.device)
+    _check(dsum, "dsum", torch.float32, (B, H, N), q.device)
+    return B, H, N, d
+
+
+def bwd_dkdv(q, k, v, do, lse, dsum, scale=None, causal=False, blockmask=None, mask_block=128,
+             dk=None, dv=None):
+    """Stage 2 of the backward: dK, dV (needs D from bwd_dsum)."""
+    torch = _torch()
+    B, H, N, d = _stage_inputs(q, k, v, do, lse, dsum)
+    scale = default_scale(d) if scale is None else float(scale)
+    dk = torch.empty_like(q) if dk is None else dk
+    dv = torch.empty_like(q) if dv is None else dv
+    _check(dk, "dk", torch.bfloat16, q.shape, q.device)
+    _check(dv, "dv", torch.bfloat16, q.shape, q.device)
+    bm_ptr, mb = _mask_args(blockmask, N, mask_block, q.device)
+    rc = load_library().fa_bwd_dkdv(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                                    lse.data_ptr(), dsum.data_ptr(), B, H, N, d, scale,
+                                    int(bool(causal)), bm_ptr, mb, dk.data_ptr(), dv.data_ptr(),
+                                    _stream_ptr(q.device))
+    if rc != FA_OK:
+        raise LibfaError(rc, "fa_bwd_dkdv")
+    return dk, dv
+
+
+def bwd_dq(q, k, v, do, lse, dsum, scale=None, causal=False, blockmask=None, mask_block=128,
+           dq=None):
+    """Stage 3 of the backward: dQ (needs D from bwd_dsum)."""
+    torch = _torch()
+    B, H, N, d = _stage_inputs(q, k, v, do, lse, dsum)
+    scale = default_scale(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    _check(dq, "dq", torch.bfloat16, q.shape, q.device)
+    bm_ptr, mb = _mask_args(blockmask, N, mask_block, q.device)
+    rc = load_library().fa_bwd_dq(q.data_ptr(), k.data_ptr(), v.data_ptr(), do.data_ptr(),
+                                  lse.data_ptr(), dsum.data_ptr(), B, H, N, d, scale,
+                                  int(bool(causal)), bm_ptr, mb, dq.data_ptr(),
+                                  _stream_ptr(q.device))
+    if rc != FA_OK:
+        raise LibfaError(rc, "fa_bwd_dq")
+    return dq
 
 
 class FlashAttention:

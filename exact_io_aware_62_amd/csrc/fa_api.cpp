@@ -8,6 +8,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 
 #include "fa_launch.hpp"
 
@@ -18,21 +19,63 @@ constexpr long long kMaxI32 = 2147483647LL;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Shared validation of shapes, scalars and masks.  Sets *empty when there is
-// nothing to compute.
-int check_common(int B, int H, int N, int d, float scale, const uint8_t* blockmask,
-                 int mask_block, bool* empty) {
+// Shapes only.  Sets *empty when there is nothing to compute.
+int check_shape(int B, int H, int N, int d, bool* empty) {
   if (B < 0 || H < 0 || N < 0 || d < 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_UNSUPPORTED;
-  if (blockmask != nullptr && (mask_block <= 0 || mask_block % 128 != 0))
-    return FA_ERR_UNSUPPORTED;
   if ((long long)N * d > kMaxI32) return FA_ERR_UNSUPPORTED;
   const long long nqb = ((long long)N + 127) / 128;
   if (nqb * B * H > kMaxI32) return FA_ERR_UNSUPPORTED;
+  if ((long long)B * H * N > kMaxI32) return FA_ERR_UNSUPPORTED;
   *empty = (long long)B * H * N == 0;
   return FA_OK;
 }
+
+// Shapes, scale and mask arguments.
+int check_common(int B, int H, int N, int d, float scale, const uint8_t* blockmask,
+                 int mask_block, bool* empty) {
+  const int rc = check_shape(B, H, N, d, empty);
+  if (rc != FA_OK) return rc;
+  if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_UNSUPPORTED;
+  if (blockmask != nullptr && (mask_block <= 0 || mask_block % 128 != 0))
+    return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+bool all_aligned16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (!aligned(p, 16)) return false;
+  return true;
+}
+
+fa::BwdParams bwd_params(const void* Q, const void* K, const void* V, const void* O,
+                         const void* dO, const float* LSE, float* Dsum, int B, int H, int N,
+                         float scale, const uint8_t* blockmask, int mask_block, void* dQ,
+                         void* dK, void* dV) {
+  fa::BwdParams p;
+  p.Q = static_cast<const uint16_t*>(Q);
+  p.K = static_cast<const uint16_t*>(K);
+  p.V = static_cast<const uint16_t*>(V);
+  p.O = static_cast<const uint16_t*>(O);
+  p.dO = static_cast<const uint16_t*>(dO);
+  p.LSE = LSE;
+  p.Dsum = Dsum;
+  p.dQ = static_cast<uint16_t*>(dQ);
+  p.dK = static_cast<uint16_t*>(dK);
+  p.dV = static_cast<uint16_t*>(dV);
+  p.blockmask = blockmask;
+  p.BH = B * H;
+  p.N = N;
+  p.nqb = (N + 127) / 128;
+  p.nkb = (N + 127) / 128;
+  p.mask_block = blockmask ? mask_block : 128;
+  p.nbm = (N + p.mask_block - 1) / p.mask_block;
+  p.scale = scale;
+  p.scale_log2 = scale * kLog2e;
+  return p;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
 }  // namespace
 
@@ -60,9 +103,7 @@ int fa_fwd(const void* Q, const void* K, const void* V, int B, int H, int N, int
   if (rc != FA_OK) return rc;
   if (empty) return FA_OK;
   if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
-  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
-      !aligned(LSE, 4))
-    return FA_ERR_UNSUPPORTED;
+  if (!all_aligned16({Q, K, V, O}) || !aligned(LSE, 4)) return FA_ERR_UNSUPPORTED;
 
   fa::FwdParams p;
   p.Q = static_cast<const uint16_t*>(Q);
@@ -77,13 +118,57 @@ int fa_fwd(const void* Q, const void* K, const void* V, int B, int H, int N, int
   p.mask_block = blockmask ? mask_block : 128;
   p.nbm = (N + p.mask_block - 1) / p.mask_block;
   p.scale_log2 = scale * kLog2e;
-  hipError_t e = fa::launch_fwd(p, d, causal != 0, blockmask != nullptr, stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  return status_of(fa::launch_fwd(p, d, causal != 0, blockmask != nullptr, stream));
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
-  if (B < 0 || H < 0 || N < 0 || (d != 64 && d != 128)) return 0;
+  bool empty = false;
+  if (check_shape(B, H, N, d, &empty) != FA_OK) return 0;
   return (size_t)4 * (size_t)B * (size_t)H * (size_t)N;
+}
+
+int fa_bwd_dsum(const void* O, const void* dO, int B, int H, int N, int d, float* Dsum,
+                hipStream_t stream) {
+  bool empty = false;
+  int rc = check_shape(B, H, N, d, &empty);
+  if (rc != FA_OK) return rc;
+  if (empty) return FA_OK;
+  if (!O || !dO || !Dsum) return FA_ERR_NULL;
+  if (!all_aligned16({O, dO}) || !aligned(Dsum, 4)) return FA_ERR_UNSUPPORTED;
+  const fa::BwdParams p = bwd_params(nullptr, nullptr, nullptr, O, dO, nullptr, Dsum, B, H, N,
+                                     1.f, nullptr, 128, nullptr, nullptr, nullptr);
+  return status_of(fa::launch_bwd_dsum(p, d, stream));
+}
+
+int fa_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+                const float* Dsum, int B, int H, int N, int d, float scale, int causal,
+                const uint8_t* blockmask, int mask_block, void* dK, void* dV,
+                hipStream_t stream) {
+  bool empty = false;
+  int rc = check_common(B, H, N, d, scale, blockmask, mask_block, &empty);
+  if (rc != FA_OK) return rc;
+  if (empty) return FA_OK;
+  if (!Q || !K || !V || !dO || !LSE || !Dsum || !dK || !dV) return FA_ERR_NULL;
+  if (!all_aligned16({Q, K, V, dO, dK, dV}) || !aligned(LSE, 4) || !aligned(Dsum, 4))
+    return FA_ERR_UNSUPPORTED;
+  const fa::BwdParams p = bwd_params(Q, K, V, nullptr, dO, LSE, const_cast<float*>(Dsum), B, H,
+                                     N, scale, blockmask, mask_block, nullptr, dK, dV);
+  return status_of(fa::launch_bwd_dkdv(p, d, causal != 0, blockmask != nullptr, stream));
+}
+
+int fa_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
+              const float* Dsum, int B, int H, int N, int d, float scale, int causal,
+              const uint8_t* blockmask, int mask_block, void* dQ, hipStream_t stream) {
+  bool empty = false;
+  int rc = check_common(B, H, N, d, scale, blockmask, mask_block, &empty);
+  if (rc != FA_OK) return rc;
+  if (empty) return FA_OK;
+  if (!Q || !K || !V || !dO || !LSE || !Dsum || !dQ) return FA_ERR_NULL;
+  if (!all_aligned16({Q, K, V, dO, dQ}) || !aligned(LSE, 4) || !aligned(Dsum, 4))
+    return FA_ERR_UNSUPPORTED;
+  const fa::BwdParams p = bwd_params(Q, K, V, nullptr, dO, LSE, const_cast<float*>(Dsum), B, H,
+                                     N, scale, blockmask, mask_block, dQ, nullptr, nullptr);
+  return status_of(fa::launch_bwd_dq(p, d, causal != 0, blockmask != nullptr, stream));
 }
 
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
@@ -97,33 +182,15 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
   if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL;
   if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d))
     return FA_ERR_WORKSPACE;
-  if (!aligned(Q, 16) || !aligned(K, 16) || !aligned(V, 16) || !aligned(O, 16) ||
-      !aligned(dO, 16) || !aligned(dQ, 16) || !aligned(dK, 16) || !aligned(dV, 16) ||
-      !aligned(LSE, 4) || !aligned(workspace, 4))
+  if (!all_aligned16({Q, K, V, O, dO, dQ, dK, dV}) || !aligned(LSE, 4) || !aligned(workspace, 4))
     return FA_ERR_UNSUPPORTED;
-
-  fa::BwdParams p;
-  p.Q = static_cast<const uint16_t*>(Q);
-  p.K = static_cast<const uint16_t*>(K);
-  p.V = static_cast<const uint16_t*>(V);
-  p.O = static_cast<const uint16_t*>(O);
-  p.dO = static_cast<const uint16_t*>(dO);
-  p.LSE = LSE;
-  p.Dsum = static_cast<float*>(workspace);
-  p.dQ = static_cast<uint16_t*>(dQ);
-  p.dK = static_cast<uint16_t*>(dK);
-  p.dV = static_cast<uint16_t*>(dV);
-  p.blockmask = blockmask;
-  p.BH = B * H;
-  p.N = N;
-  p.nqb = (N + 127) / 128;
-  p.nkb = (N + 127) / 128;
-  p.mask_block = blockmask ? mask_block : 128;
-  p.nbm = (N + p.mask_block - 1) / p.mask_block;
-  p.scale = scale;
-  p.scale_log2 = scale * kLog2e;
-  hipError_t e = fa::launch_bwd(p, d, causal != 0, blockmask != nullptr, stream);
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+  const fa::BwdParams p = bwd_params(Q, K, V, O, dO, LSE, static_cast<float*>(workspace), B, H,
+                                     N, scale, blockmask, mask_block, dQ, dK, dV);
+  const bool cz = causal != 0, sp = blockmask != nullptr;
+  rc = status_of(fa::launch_bwd_dsum(p, d, stream));
+  if (rc == FA_OK) rc = status_of(fa::launch_bwd_dkdv(p, d, cz, sp, stream));
+  if (rc == FA_OK) rc = status_of(fa::launch_bwd_dq(p, d, cz, sp, stream));
+  return rc;
 }
 
 }  // extern "C"

@@ -389,34 +389,51 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdParams p) {
   }
 }
 
-template <int D, bool CAUSAL, bool SPARSE>
-static hipError_t launch_bwd_t(const BwdParams& p, hipStream_t stream) {
+hipError_t launch_bwd_dsum(const BwdParams& p, int d, hipStream_t stream) {
   const long long rows = (long long)p.BH * p.N;
-  constexpr int RPB = 256 / (D / 8);
-  hipLaunchKernelGGL((dsum_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
-                     stream, p, rows);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (d == 64) {
+    constexpr int RPB = 256 / (64 / 8);
+    hipLaunchKernelGGL((dsum_kernel<64>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                       stream, p, rows);
+  } else {
+    constexpr int RPB = 256 / (128 / 8);
+    hipLaunchKernelGGL((dsum_kernel<128>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256),
+                       0, stream, p, rows);
+  }
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool SPARSE>
+static hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, SPARSE>), dim3((unsigned)((long long)p.nkb * p.BH)),
                      dim3(256), 0, stream, p);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  return hipGetLastError();
+}
+
+template <int D, bool CAUSAL, bool SPARSE>
+static hipError_t launch_dq_t(const BwdParams& p, hipStream_t stream) {
   hipLaunchKernelGGL((dq_kernel<D, CAUSAL, SPARSE>), dim3((unsigned)((long long)p.nqb * p.BH)),
                      dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd(const BwdParams& p, int d, bool causal, bool sparse, hipStream_t stream) {
-  if (d == 64) {
-    if (causal) return sparse ? launch_bwd_t<64, true, true>(p, stream)
-                              : launch_bwd_t<64, true, false>(p, stream);
-    return sparse ? launch_bwd_t<64, false, true>(p, stream)
-                  : launch_bwd_t<64, false, false>(p, stream);
-  }
-  if (causal) return sparse ? launch_bwd_t<128, true, true>(p, stream)
-                            : launch_bwd_t<128, true, false>(p, stream);
-  return sparse ? launch_bwd_t<128, false, true>(p, stream)
-                : launch_bwd_t<128, false, false>(p, stream);
+#define FA_DISPATCH(FN, d, causal, sparse, ...)                                           \
+  ((d) == 64 ? ((causal) ? ((sparse) ? FN<64, true, true>(__VA_ARGS__)                    \
+                                     : FN<64, true, false>(__VA_ARGS__))                  \
+                         : ((sparse) ? FN<64, false, true>(__VA_ARGS__)                   \
+                                     : FN<64, false, false>(__VA_ARGS__)))                \
+             : ((causal) ? ((sparse) ? FN<128, true, true>(__VA_ARGS__)                   \
+                                     : FN<128, true, false>(__VA_ARGS__))                 \
+                         : ((sparse) ? FN<128, false, true>(__VA_ARGS__)                  \
+                                     : FN<128, false, false>(__VA_ARGS__))))
+
+hipError_t launch_bwd_dkdv(const BwdParams& p, int d, bool causal, bool sparse,
+                           hipStream_t stream) {
+  return FA_DISPATCH(launch_dkdv_t, d, causal, sparse, p, stream);
+}
+
+hipError_t launch_bwd_dq(const BwdParams& p, int d, bool causal, bool sparse, hipStream_t stream) {
+  return FA_DISPATCH(launch_dq_t, d, causal, sparse, p, stream);
 }
 
 }  // namespace fa

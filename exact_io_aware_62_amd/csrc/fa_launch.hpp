@@ -45,6 +45,9 @@ struct BwdParams {
 };
 
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool sparse, hipStream_t stream);
-hipError_t launch_bwd(const BwdParams& p, int d, bool causal, bool sparse, hipStream_t stream);
+hipError_t launch_bwd_dsum(const BwdParams& p, int d, hipStream_t stream);
+hipError_t launch_bwd_dkdv(const BwdParams& p, int d, bool causal, bool sparse,
+                           hipStream_t stream);
+hipError_t launch_bwd_dq(const BwdParams& p, int d, bool causal, bool sparse, hipStream_t stream);
 
 }  // namespace fa

@@ -43,7 +43,8 @@
  *   d in {64, 128}; N >= 0 (any length; a partial last tile is masked);
  *   scale finite and > 0; mask_block a positive multiple of 128 when
  *   blockmask != NULL (ignored otherwise); N * d < 2^31 and
- *   ceil(N / 128) * B * H < 2^31.
+ *   ceil(N / 128) * B * H < 2^31; bf16 tensor pointers 16-byte aligned,
+ *   float32 pointers 4-byte aligned.
  *   B, H or N equal to 0 is a valid empty problem: nothing is launched.
  *
  * Errors.  Every argument check happens before any HIP call, and on error
@@ -127,6 +128,31 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
            const uint8_t* blockmask, int mask_block,
            void* dQ, void* dK, void* dV,
            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The three stages of fa_bwd as separate calls, for callers that schedule
+ * them themselves (for example fa_bwd_dkdv and fa_bwd_dq on two streams once
+ * fa_bwd_dsum has finished: they read the same inputs and write disjoint
+ * outputs).  fa_bwd is exactly fa_bwd_dsum, then fa_bwd_dkdv, then fa_bwd_dq
+ * on one stream.  Arguments mean what they mean for fa_bwd; Dsum is the
+ * float32 [B, H, N] buffer of D_i = sum_k dO_ik * O_ik (the workspace of
+ * fa_bwd), written by fa_bwd_dsum and read by the other two.  Same errors
+ * as fa_bwd, with FA_ERR_NULL for a NULL Dsum.
+ */
+int fa_bwd_dsum(const void* O, const void* dO, int B, int H, int N, int d,
+                float* Dsum, hipStream_t stream);
+
+int fa_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO,
+                const float* LSE, const float* Dsum,
+                int B, int H, int N, int d, float scale, int causal,
+                const uint8_t* blockmask, int mask_block,
+                void* dK, void* dV, hipStream_t stream);
+
+int fa_bwd_dq(const void* Q, const void* K, const void* V, const void* dO,
+              const float* LSE, const float* Dsum,
+              int B, int H, int N, int d, float scale, int causal,
+              const uint8_t* blockmask, int mask_block,
+              void* dQ, hipStream_t stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_strerror(int status);
