@@ -135,7 +135,20 @@ def main():
     ap.add_argument("--workload", default="C3", choices=sorted(synth.CONFIGS))
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the oracle timed on host cores (0 disables it)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy three times (a "
+                         "known-size reference for the HBM byte counters) and exit")
     args = ap.parse_args()
+    if args.copy_calibration:
+        import torch
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] copy calibration: 3 copies of 1 GiB done")
+        return
     if args.gpus != 1:
         log(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
             "supported (heads shard across GPUs with no exchange; see the design notes).")

@@ -18,6 +18,8 @@
 // Both main kernels split the sequence over workgroups the way the forward
 // does (FlashAttention-2 wiki, "技术架构与工作原理", item 2).
 
+#include <type_traits>
+
 #include "fa_common.hpp"
 #include "fa_launch.hpp"
 
@@ -58,30 +60,27 @@ __global__ __launch_bounds__(256) void dsum_kernel(BwdParams p, long long rows) 
 // ---------------------------------------------------------------------------
 // 2. dK, dV.  Workgroup = 4 wavefronts = 128 keys; wavefront w owns keys
 //    kw .. kw+31 and keeps K and V rows for them in registers.  Query tiles
-//    of 64 rows stream through LDS (double-buffered) in two layouts: natural
-//    (for S = Q K^T and dP = dO V^T, contraction over d) and transposed (for
-//    dV^T += dO^T P and dK^T += Q^T dS, contraction over queries).
-//    Scores are formed as S (queries x keys) so each lane owns one key and
-//    the P / dS fragments feed the dV / dK products as B operands directly.
+//    of 64 rows (Q and dO, natural layout) are copied HBM -> LDS
+//    asynchronously, double-buffered.  S = Q K^T and dP = dO V^T contract
+//    over d (row operands); dV^T += dO^T P and dK^T += Q^T dS contract over
+//    queries, with dO^T and Q^T read by the LDS transpose read.  Scores are
+//    formed as S (queries x keys) so each lane owns one key and the P / dS
+//    fragments feed the dV / dK products as B operands directly.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
-  constexpr int BKB = 128, BQ = 64, NT = 256;
+  constexpr int BKB = 128, BQ = 64, NW = 4;
   constexpr int NDB = D / 32, NKK = D / 16, NQB = BQ / 32;
-  using NStage = NaturalStage<BQ, D, NT>;
-  using TStage = TransposedStage<BQ, D, NT>;
-  constexpr int NS = NStage::kStride, TS = TStage::kStride;
-  // per buffer: Q, dO natural; Q, dO transposed; lse2[BQ]; D[BQ]
-  constexpr int OFF_QN = 0;
-  constexpr int OFF_ON = OFF_QN + NStage::kElems;
-  constexpr int OFF_QT = OFF_ON + NStage::kElems;
-  constexpr int OFF_OT = OFF_QT + TStage::kElems;
-  constexpr int OFF_ROW = OFF_OT + TStage::kElems;   // 2 * BQ floats
-  constexpr int BUF = OFF_ROW + 2 * BQ * 2;          // in uint16 units
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BUF];
+  using T = LdsTile<BQ, D>;
+  constexpr int RB = T::kRowBytes;
+  // per stage: Q tile, dO tile, lse2[BQ] and D[BQ] (padded to 1 KB)
+  constexpr int OFF_Q = 0, OFF_O = T::kBytes, OFF_ROW = 2 * T::kBytes;
+  constexpr int STAGE = 2 * T::kBytes + 1024;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, r = lane & 31, g = lane >> 5;
+  const int lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const BlockCoord bc = block_coord(p.BH);
   const int kb = bc.blk;
   const int N = p.N;
@@ -91,8 +90,8 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   const float* __restrict__ lseh = p.LSE + (size_t)bc.bh * N;
   const float* __restrict__ Dh = p.Dsum + (size_t)bc.bh * N;
 
-  const int kw = kb * BKB + w * 32;   // first key of this wavefront
-  const int key = kw + r;             // this lane's key
+  const int kw = kb * BKB + wave * 32;   // first key of this wavefront
+  const int key = kw + r;                // this lane's key
   bf16x8 kf[NKK], vf[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
@@ -105,12 +104,10 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   const int nqt = (N + BQ - 1) / BQ;
   const int t_begin = CAUSAL ? (kb * BKB) / BQ : 0;
   const int mcol = SPARSE ? (kb * BKB) / p.mask_block : 0;
-  auto active = [&](int t) -> bool {
-    if (!SPARSE) return true;
-    return p.blockmask[(size_t)((t * BQ) / p.mask_block) * p.nbm + mcol] != 0;
-  };
   auto next_tile = [&](int t) -> int {
-    while (t < nqt && !active(t)) ++t;
+    if constexpr (SPARSE) {
+      while (t < nqt && p.blockmask[(size_t)((t * BQ) / p.mask_block) * p.nbm + mcol] == 0) ++t;
+    }
     return t;
   };
 
@@ -122,14 +119,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   }
   const float c = p.scale_log2;
 
-  NStage qn, on;
-  TStage qt, ot;
-  float rowv = 0.f;   // thread tid < 2*BQ stages one lse2 / D value
-  auto load_tile = [&](int t) {
-    qn.load(Qh, t * BQ, N, tid);
-    on.load(dOh, t * BQ, N, tid);
-    qt.load(Qh, t * BQ, N, tid);
-    ot.load(dOh, t * BQ, N, tid);
+  float rowv = 0.f;   // thread tid < 2*BQ carries one lse2 / D value of the next tile
+  auto issue = [&](int t, int bufi) {
+    char* st = lds + bufi * STAGE;
+    T::template copy<NW>(Qh, t * BQ, N, st + OFF_Q, wave, lane);
+    T::template copy<NW>(dOh, t * BQ, N, st + OFF_O, wave, lane);
     if (tid < 2 * BQ) {
       const int q = t * BQ + (tid % BQ);
       if (tid < BQ)
@@ -138,87 +132,94 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
         rowv = q < N ? Dh[q] : 0.f;
     }
   };
-  auto store_tile = [&](uint16_t* b) {
-    qn.store(b + OFF_QN, tid);
-    on.store(b + OFF_ON, tid);
-    qt.store(b + OFF_QT, tid);
-    ot.store(b + OFF_OT, tid);
-    if (tid < 2 * BQ) reinterpret_cast<float*>(b + OFF_ROW)[tid] = rowv;
+  auto finish_issue = [&](int bufi) {
+    if (tid < 2 * BQ) reinterpret_cast<float*>(lds + bufi * STAGE + OFF_ROW)[tid] = rowv;
+  };
+
+  auto compute = [&](auto bufc, int t) {
+    constexpr int BUFI = decltype(bufc)::value;
+    const char* st = lds + BUFI * STAGE;
+    const char* qt = st + OFF_Q;
+    const char* ot = st + OFF_O;
+    const float* lse2 = reinterpret_cast<const float*>(st + OFF_ROW);
+    const float* dsum = lse2 + BQ;
+    const int q0 = t * BQ;
+    if (CAUSAL && q0 + BQ - 1 < kw) return;   // every query of the tile precedes our keys
+    // S = Q K^T and dP = dO V^T for NQB blocks of 32 queries
+    f32x16 s[NQB], dp[NQB];
+#pragma unroll
+    for (int qb2 = 0; qb2 < NQB; ++qb2) {
+      s[qb2] = zero16();
+      dp[qb2] = zero16();
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk) {
+        s[qb2] = mfma32x32x16(lds_row_operand<T>(qt + qb2 * 32 * RB, r, 2 * kk + g), kf[kk],
+                              s[qb2]);
+        dp[qb2] = mfma32x32x16(lds_row_operand<T>(ot + qb2 * 32 * RB, r, 2 * kk + g), vf[kk],
+                               dp[qb2]);
+      }
+    }
+    const bool need_mask = (CAUSAL && q0 < kw + 31) || (q0 + BQ > N) || (kw + 32 > N);
+    // P = exp2(S * c - lse2[q]);  dS = P * (dP - D[q])
+#pragma unroll
+    for (int qb2 = 0; qb2 < NQB; ++qb2)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int ql = qb2 * 32 + i4 * 8 + g * 4;   // local query of register i4*4
+        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + ql);
+        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dsum + ql);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int i = i4 * 4 + j;
+          float sv = s[qb2][i];
+          if (need_mask) {
+            const int q = q0 + ql + j;
+            if ((CAUSAL && key > q) || q >= N || key >= N) sv = -INFINITY;
+          }
+          const float pv = exp2_fast(__builtin_fmaf(sv, c, -l4[j]));
+          s[qb2][i] = pv;
+          dp[qb2][i] = pv * (dp[qb2][i] - d4[j]);
+        }
+      }
+    // dV^T += dO^T P ;  dK^T += Q^T dS   (contraction over queries)
+#pragma unroll
+    for (int qb2 = 0; qb2 < NQB; ++qb2)
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        const bf16x8 pb = pack_c8(s[qb2], 8 * ks2);
+        const bf16x8 sb = pack_c8(dp[qb2], 8 * ks2);
+        const int rb = (qb2 * 32 + 16 * ks2) * RB;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const int o0 = tr_offset<T>(0, db * 32, lane, 0), o1 = tr_offset<T>(0, db * 32, lane, 1);
+          const bf16x8 ao = bf16x8_from_halves(lds_tr_b64(ot + rb + o0), lds_tr_b64(ot + rb + o1));
+          dv[db] = mfma32x32x16(ao, pb, dv[db]);
+          const bf16x8 aq = bf16x8_from_halves(lds_tr_b64(qt + rb + o0), lds_tr_b64(qt + rb + o1));
+          dk[db] = mfma32x32x16(aq, sb, dk[db]);
+        }
+      }
   };
 
   int t = next_tile(t_begin);
   if (t < nqt) {
-    load_tile(t);
-    store_tile(lds);
+    issue(t, 0);
+    finish_issue(0);
   }
-  int buf = 0;
   while (t < nqt) {
+    wait_vmem();
     __syncthreads();
-    const int tn = next_tile(t + 1);
-    if (tn < nqt) load_tile(tn);
-    const uint16_t* b = lds + buf * BUF;
-    const float* lse2 = reinterpret_cast<const float*>(b + OFF_ROW);
-    const float* dsum = lse2 + BQ;
-    const int q0 = t * BQ;
-    const bool live = !CAUSAL || q0 + BQ - 1 >= kw;
-    if (live) {
-      // S = Q K^T and dP = dO V^T for NQB blocks of 32 queries
-      f32x16 s[NQB], dp[NQB];
-#pragma unroll
-      for (int qb2 = 0; qb2 < NQB; ++qb2) {
-        s[qb2] = zero16();
-        dp[qb2] = zero16();
-#pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          s[qb2] = mfma32x32x16(lds_row8(b + OFF_QN, NS, qb2 * 32 + r, kk * 16 + g * 8), kf[kk],
-                                s[qb2]);
-          dp[qb2] = mfma32x32x16(lds_row8(b + OFF_ON, NS, qb2 * 32 + r, kk * 16 + g * 8), vf[kk],
-                                 dp[qb2]);
-        }
-      }
-      const bool need_mask = (CAUSAL && q0 < kw + 31) || (q0 + BQ > N) || (kw + 32 > N);
-      // P = exp2(S * c - lse2[q]);  dS = P * (dP - D[q])
-#pragma unroll
-      for (int qb2 = 0; qb2 < NQB; ++qb2)
-#pragma unroll
-        for (int i4 = 0; i4 < 4; ++i4) {
-          const int ql = qb2 * 32 + i4 * 8 + g * 4;   // local query of register i4*4
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + ql);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(dsum + ql);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const int i = i4 * 4 + j;
-            float sv = s[qb2][i];
-            if (need_mask) {
-              const int q = q0 + ql + j;
-              if ((CAUSAL && key > q) || q >= N || key >= N) sv = -INFINITY;
-            }
-            const float pv = exp2_fast(__builtin_fmaf(sv, c, -l4[j]));
-            s[qb2][i] = pv;
-            dp[qb2][i] = pv * (dp[qb2][i] - d4[j]);
-          }
-        }
-      // dV^T += dO^T P ;  dK^T += Q^T dS   (contraction over queries)
-#pragma unroll
-      for (int qb2 = 0; qb2 < NQB; ++qb2)
-#pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2) {
-          const int e = 8 * ks2;
-          const bf16x8 pb = pack_bf16x8(s[qb2][e + 0], s[qb2][e + 1], s[qb2][e + 2], s[qb2][e + 3],
-                                        s[qb2][e + 4], s[qb2][e + 5], s[qb2][e + 6], s[qb2][e + 7]);
-          const bf16x8 sb =
-              pack_bf16x8(dp[qb2][e + 0], dp[qb2][e + 1], dp[qb2][e + 2], dp[qb2][e + 3],
-                          dp[qb2][e + 4], dp[qb2][e + 5], dp[qb2][e + 6], dp[qb2][e + 7]);
-          const int c0 = qb2 * 32 + 16 * ks2 + g * 4;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db) {
-            dv[db] = mfma32x32x16(lds_tr8(b + OFF_OT, TS, db * 32 + r, c0, c0 + 8), pb, dv[db]);
-            dk[db] = mfma32x32x16(lds_tr8(b + OFF_QT, TS, db * 32 + r, c0, c0 + 8), sb, dk[db]);
-          }
-        }
-    }
-    if (tn < nqt) store_tile(lds + (buf ^ 1) * BUF);
-    buf ^= 1;
+    int tn = next_tile(t + 1);
+    if (tn < nqt) issue(tn, 1);
+    compute(std::integral_constant<int, 0>{}, t);
+    if (tn < nqt) finish_issue(1);
+    t = tn;
+    if (t >= nqt) break;
+    wait_vmem();
+    __syncthreads();
+    tn = next_tile(t + 1);
+    if (tn < nqt) issue(tn, 0);
+    compute(std::integral_constant<int, 1>{}, t);
+    if (tn < nqt) finish_issue(0);
     t = tn;
   }
 
@@ -245,26 +246,25 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
 
 // ---------------------------------------------------------------------------
 // 3. dQ.  Workgroup = 4 wavefronts = 128 query rows (32 per wavefront, held
-//    in registers with their dO rows).  Key tiles of 64 rows stream through
-//    LDS: K natural (S^T = K Q^T), V natural (dP^T = V dO^T) and K transposed
-//    (dQ^T += K^T dS^T).  Same transposed-score arrangement as the forward:
-//    each lane owns one query row, so LSE and D are per-lane scalars.
+//    in registers with their dO rows).  Key tiles of 64 rows (K and V,
+//    natural layout) are copied HBM -> LDS asynchronously, double-buffered:
+//    S^T = K Q^T and dP^T = V dO^T use row operands, dQ^T += K^T dS^T reads
+//    K^T with the LDS transpose read.  Same transposed-score arrangement as
+//    the forward: each lane owns one query row, so LSE and D are per-lane
+//    scalars.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(256, 1) void dq_kernel(BwdParams p) {
-  constexpr int BQ = 128, BK = 64, NT = 256;
+__global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
+  constexpr int BQ = 128, BK = 64, NW = 4;
   constexpr int NDB = D / 32, NKK = D / 16;
-  using NStage = NaturalStage<BK, D, NT>;
-  using TStage = TransposedStage<BK, D, NT>;
-  constexpr int NS = NStage::kStride, TS = TStage::kStride;
-  constexpr int OFF_KN = 0;
-  constexpr int OFF_VN = OFF_KN + NStage::kElems;
-  constexpr int OFF_KT = OFF_VN + NStage::kElems;
-  constexpr int BUF = OFF_KT + TStage::kElems;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BUF];
+  using T = LdsTile<BK, D>;
+  constexpr int RB = T::kRowBytes;
+  constexpr int STAGE = 2 * T::kBytes;   // K tile, then V tile
+  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, w = tid >> 6, r = lane & 31, g = lane >> 5;
+  const int lane = tid & 63, r = lane & 31, g = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const BlockCoord bc = block_coord(p.BH);
   const int qb = CAUSAL ? (p.nqb - 1 - bc.blk) : bc.blk;
   const int N = p.N;
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdParams p) {
   const uint16_t* __restrict__ Kh = p.K + head;
   const uint16_t* __restrict__ Vh = p.V + head;
 
-  const int q0w = qb * BQ + w * 32;
+  const int q0w = qb * BQ + wave * 32;
   const int qrow = q0w + r;
   bf16x8 qf[NKK], of[NKK];
 #pragma unroll
@@ -287,12 +287,11 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdParams p) {
   const int kend = CAUSAL ? min(N, (qb + 1) * BQ) : N;
   const int ntiles = (kend + BK - 1) / BK;
   const int mrow = SPARSE ? (qb * BQ) / p.mask_block : 0;
-  auto active = [&](int t) -> bool {
-    if (!SPARSE) return true;
-    return p.blockmask[(size_t)mrow * p.nbm + (t * BK) / p.mask_block] != 0;
-  };
   auto next_tile = [&](int t) -> int {
-    while (t < ntiles && !active(t)) ++t;
+    if constexpr (SPARSE) {
+      const uint8_t* mr = p.blockmask + (size_t)mrow * p.nbm;
+      while (t < ntiles && mr[(t * BK) / p.mask_block] == 0) ++t;
+    }
     return t;
   };
 
@@ -301,78 +300,74 @@ __global__ __launch_bounds__(256, 1) void dq_kernel(BwdParams p) {
   for (int db = 0; db < NDB; ++db) dq[db] = zero16();
   const float c = p.scale_log2;
 
-  NStage kn, vn;
-  TStage kt;
-  int t = next_tile(0);
-  if (t < ntiles) {
-    kn.load(Kh, t * BK, N, tid);
-    vn.load(Vh, t * BK, N, tid);
-    kt.load(Kh, t * BK, N, tid);
-    kn.store(lds + OFF_KN, tid);
-    vn.store(lds + OFF_VN, tid);
-    kt.store(lds + OFF_KT, tid);
-  }
-  int buf = 0;
-  while (t < ntiles) {
-    __syncthreads();
-    const int tn = next_tile(t + 1);
-    if (tn < ntiles) {
-      kn.load(Kh, tn * BK, N, tid);
-      vn.load(Vh, tn * BK, N, tid);
-      kt.load(Kh, tn * BK, N, tid);
-    }
-    const uint16_t* b = lds + buf * BUF;
+  auto issue = [&](int t, int bufi) {
+    char* st = lds + bufi * STAGE;
+    T::template copy<NW>(Kh, t * BK, N, st, wave, lane);
+    T::template copy<NW>(Vh, t * BK, N, st + T::kBytes, wave, lane);
+  };
+
+  auto compute = [&](auto bufc, int t) {
+    constexpr int BUFI = decltype(bufc)::value;
+    const char* kt = lds + BUFI * STAGE;
+    const char* vt = kt + T::kBytes;
     const int k0 = t * BK;
-    const bool live = !CAUSAL || k0 <= q0w + 31;
-    if (live) {
-      f32x16 s[2], dp[2];
+    if (CAUSAL && k0 > q0w + 31) return;
+    f32x16 s[2], dp[2];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = zero16();
-        dp[kb] = zero16();
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = zero16();
+      dp[kb] = zero16();
 #pragma unroll
-        for (int kk = 0; kk < NKK; ++kk) {
-          s[kb] = mfma32x32x16(lds_row8(b + OFF_KN, NS, kb * 32 + r, kk * 16 + g * 8), qf[kk],
-                               s[kb]);
-          dp[kb] = mfma32x32x16(lds_row8(b + OFF_VN, NS, kb * 32 + r, kk * 16 + g * 8), of[kk],
-                                dp[kb]);
+      for (int kk = 0; kk < NKK; ++kk) {
+        s[kb] = mfma32x32x16(lds_row_operand<T>(kt + kb * 32 * RB, r, 2 * kk + g), qf[kk], s[kb]);
+        dp[kb] = mfma32x32x16(lds_row_operand<T>(vt + kb * 32 * RB, r, 2 * kk + g), of[kk],
+                              dp[kb]);
+      }
+    }
+    const bool need_mask = (CAUSAL && k0 + BK - 1 > q0w) || (k0 + BK > N);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        float sv = s[kb][i];
+        if (need_mask) {
+          const int key = k0 + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
+          if (key >= N || (CAUSAL && key > qrow)) sv = -INFINITY;
+        }
+        const float pv = exp2_fast(__builtin_fmaf(sv, c, -lse2));
+        dp[kb][i] = pv * (dp[kb][i] - dsum);
+      }
+    // dQ^T += K^T dS^T
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) {
+        const bf16x8 sb = pack_c8(dp[kb], 8 * ks2);
+        const char* kk0 = kt + (kb * 32 + 16 * ks2) * RB;
+#pragma unroll
+        for (int db = 0; db < NDB; ++db) {
+          const bf16x8 a = bf16x8_from_halves(lds_tr_b64(kk0 + tr_offset<T>(0, db * 32, lane, 0)),
+                                              lds_tr_b64(kk0 + tr_offset<T>(0, db * 32, lane, 1)));
+          dq[db] = mfma32x32x16(a, sb, dq[db]);
         }
       }
-      const bool need_mask = (CAUSAL && k0 + BK - 1 > q0w) || (k0 + BK > N);
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float sv = s[kb][i];
-          if (need_mask) {
-            const int key = k0 + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-            if (key >= N || (CAUSAL && key > qrow)) sv = -INFINITY;
-          }
-          const float pv = exp2_fast(__builtin_fmaf(sv, c, -lse2));
-          dp[kb][i] = pv * (dp[kb][i] - dsum);
-        }
-      // dQ^T += K^T dS^T
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int ks2 = 0; ks2 < 2; ++ks2) {
-          const int e = 8 * ks2;
-          const bf16x8 sb =
-              pack_bf16x8(dp[kb][e + 0], dp[kb][e + 1], dp[kb][e + 2], dp[kb][e + 3],
-                          dp[kb][e + 4], dp[kb][e + 5], dp[kb][e + 6], dp[kb][e + 7]);
-          const int c0 = kb * 32 + 16 * ks2 + g * 4;
-#pragma unroll
-          for (int db = 0; db < NDB; ++db)
-            dq[db] = mfma32x32x16(lds_tr8(b + OFF_KT, TS, db * 32 + r, c0, c0 + 8), sb, dq[db]);
-        }
-    }
-    if (tn < ntiles) {
-      uint16_t* nb = lds + (buf ^ 1) * BUF;
-      kn.store(nb + OFF_KN, tid);
-      vn.store(nb + OFF_VN, tid);
-      kt.store(nb + OFF_KT, tid);
-    }
-    buf ^= 1;
+  };
+
+  int t = next_tile(0);
+  if (t < ntiles) issue(t, 0);
+  while (t < ntiles) {
+    wait_vmem();
+    __syncthreads();
+    int tn = next_tile(t + 1);
+    if (tn < ntiles) issue(tn, 1);
+    compute(std::integral_constant<int, 0>{}, t);
+    t = tn;
+    if (t >= ntiles) break;
+    wait_vmem();
+    __syncthreads();
+    tn = next_tile(t + 1);
+    if (tn < ntiles) issue(tn, 0);
+    compute(std::integral_constant<int, 1>{}, t);
     t = tn;
   }
 

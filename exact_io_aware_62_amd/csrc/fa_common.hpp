@@ -1,6 +1,6 @@
 // Device-side building blocks shared by the forward and backward kernels:
-// vector types, the gfx950 bf16 matrix-core op, bf16 packing, and the
-// global -> LDS tile staging used by every kernel.
+// vector types, the gfx950 bf16 matrix-core op, bf16 packing, and the LDS
+// tile format with its HBM -> LDS copy and operand reads.
 //
 // Matrix-core fragment layout used throughout (v_mfma_f32_32x32x16_bf16,
 // one 64-lane wavefront; lane l, r = l % 32, g = l / 32):
@@ -8,8 +8,11 @@
 //   B (16 x 32):  lane l holds column n = r, the same eight (g, j) k values
 //   C (32 x 32):  lane l, register i holds C[(i/4)*8 + g*4 + i%4][r]
 // Only the C layout and "A and B agree on (g, j) -> k" are relied on, so the
-// order in which a contraction visits its k index is free; the kernels use
-// that freedom to feed a C fragment straight back in as a B operand.
+// order in which a contraction visits its k index is free.  The kernels use
+// that freedom to feed a C fragment straight back in as a B operand: for
+// k-step s of a 32-wide C block, registers 8s .. 8s+7 of lane group g hold
+// C rows (2s + j/4)*8 + g*4 + j%4, j = 0..7, and the A operand is gathered
+// in exactly that row order (see lds_tr_operand).
 
 #pragma once
 
@@ -23,6 +26,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -64,6 +71,12 @@ __device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, floa
   return r;
 }
 
+// Eight consecutive registers of a C fragment -> bf16x8 B operand.
+__device__ __forceinline__ bf16x8 pack_c8(const f32x16& c, int base) {
+  return pack_bf16x8(c[base + 0], c[base + 1], c[base + 2], c[base + 3], c[base + 4],
+                     c[base + 5], c[base + 6], c[base + 7]);
+}
+
 // Four fp32 -> four bf16 in two dwords (RNE).
 __device__ __forceinline__ u32x2 pack_bf16x4(float a0, float a1, float a2, float a3) {
   typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
@@ -74,7 +87,20 @@ __device__ __forceinline__ u32x2 pack_bf16x4(float a0, float a1, float a2, float
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
-__device__ __forceinline__ float xor32(float x) { return __shfl_xor(x, 32); }
+// max over lanes l and l ^ 32 (the two halves of a wavefront), without LDS:
+// v_permlane32_swap exchanges the upper half of one operand with the lower
+// half of the other, so the two results are {x[l], x[l ^ 32]} in some order.
+__device__ __forceinline__ float max_xor32(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float sum_xor32(float x) {
+  const unsigned u = __float_as_uint(x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -86,118 +112,86 @@ __device__ __forceinline__ u32x4 zero_u32x4() {
   return z;
 }
 
-// ---------------------------------------------------------------------------
-// Tile staging.  A tile is ROWS consecutive rows (tokens) x D columns of one
-// head of a BHND tensor.  Rows at or beyond `n_valid` are filled with zeros,
-// so a partial last tile never feeds stale bits (possibly NaN) to the matrix
-// cores.  Two LDS layouts:
-//   natural    [ROWS][D + 8]   row-major, 16-byte pad per row
-//   transposed [D][ROWS + 4]   column-major copy, 8-byte pad per row
-// Loads go HBM -> VGPR first (so they overlap compute of the previous tile),
-// then VGPR -> LDS after the compute.
-// ---------------------------------------------------------------------------
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-template <int ROWS, int D, int NT>
-struct NaturalStage {
-  static constexpr int kChunks = ROWS * D / 8;            // 16-byte chunks
-  static constexpr int kPerThread = (kChunks + NT - 1) / NT;
-  static constexpr int kStride = D + 8;                   // bf16 elements
-  static constexpr int kElems = ROWS * kStride;
-  u32x4 reg[kPerThread];
+// ---------------------------------------------------------------------------
+// LDS tile: ROWS x D bf16 (one head, consecutive tokens), row-major with no
+// padding; the sixteen-byte chunks of each row are XOR-permuted so that the
+// two access patterns the kernels use are free of bank conflicts:
+//   * operand rows: 16 lanes read the same chunk of 16 consecutive rows;
+//   * transposed operands: 16 lanes read two chunks of 4 consecutive rows.
+// The copy from HBM uses global_load_lds_dwordx4: each wavefront instruction
+// writes 64 x 16 contiguous bytes of LDS, lane l at byte 16*l, so lane l
+// fetches whichever logical chunk lives at that physical position.  Rows at
+// or past `n_valid` are fetched from row n_valid - 1 instead (valid memory,
+// finite values); every kernel masks those rows, so they never contribute.
+// ---------------------------------------------------------------------------
+template <int ROWS, int D>
+struct LdsTile {
+  static_assert(D == 64 || D == 128, "head dim");
+  static constexpr int kCPR = D / 8;                 // chunks per row
+  static constexpr int kRowBytes = D * 2;
+  static constexpr int kBytes = ROWS * kRowBytes;
+  static constexpr int kSegs = ROWS * kCPR / 64;     // 1 KB copy segments
 
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int row0,
-                                       int n_valid, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int c = tid + i * NT;
-      const int row = c / (D / 8);
-      const int col = (c % (D / 8)) * 8;
-      if ((kChunks % NT == 0 || c < kChunks) && row0 + row < n_valid)
-        reg[i] = ldg16(src + (size_t)(row0 + row) * D + col);
-      else
-        reg[i] = zero_u32x4();
-    }
+  __device__ static __forceinline__ int swz(int row) {
+    if constexpr (D == 128)
+      return ((row & 3) << 2) | ((row >> 2) & 3);
+    else
+      return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+  }
+  // byte offset of logical 16-byte chunk `chunk` of row `row`
+  __device__ static __forceinline__ int off(int row, int chunk) {
+    return row * kRowBytes + ((chunk ^ swz(row)) << 4);
   }
 
-  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
+  // The NW wavefronts of a workgroup copy rows [row0, row0 + ROWS) of `src`
+  // (row stride D) into `lds`.  Asynchronous: wait_vmem() + a barrier before
+  // the data is read.
+  template <int NW>
+  __device__ static __forceinline__ void copy(const uint16_t* __restrict__ src, int row0,
+                                              int n_valid, char* lds, int wave, int lane) {
+    static_assert(kSegs % NW == 0, "segments per wavefront");
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int c = tid + i * NT;
-      if (kChunks % NT == 0 || c < kChunks) {
-        const int row = c / (D / 8);
-        const int col = (c % (D / 8)) * 8;
-        *reinterpret_cast<u32x4*>(lds + row * kStride + col) = reg[i];
-      }
+    for (int i = 0; i < kSegs / NW; ++i) {
+      const int seg = wave + i * NW;
+      const int P = seg * 64 + lane;
+      const int row = P / kCPR;
+      const int chunk = (P % kCPR) ^ swz(row);
+      const int grow = min(row0 + row, n_valid - 1);
+      const uint16_t* g = src + (size_t)grow * D + chunk * 8;
+      __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds + seg * 1024), 16, 0, 0);
     }
   }
 };
 
-// Transposed staging: a unit is 4 rows x 8 columns; the thread loads the
-// four 16-byte row pieces and writes eight 8-byte column pieces.
-template <int ROWS, int D, int NT>
-struct TransposedStage {
-  static constexpr int kUnits = (ROWS / 4) * (D / 8);
-  static constexpr int kPerThread = (kUnits + NT - 1) / NT;
-  static constexpr int kStride = ROWS + 4;                // bf16 elements
-  static constexpr int kElems = D * kStride;
-  u32x4 reg[kPerThread][4];
-
-  __device__ __forceinline__ void load(const uint16_t* __restrict__ src, int row0,
-                                       int n_valid, int tid) {
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int u = tid + i * NT;
-      const int rg = u / (D / 8);
-      const int col = (u % (D / 8)) * 8;
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr) {
-        const int row = rg * 4 + rr;
-        if ((kUnits % NT == 0 || u < kUnits) && row0 + row < n_valid)
-          reg[i][rr] = ldg16(src + (size_t)(row0 + row) * D + col);
-        else
-          reg[i][rr] = zero_u32x4();
-      }
-    }
-  }
-
-  __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int u = tid + i * NT;
-      if (kUnits % NT == 0 || u < kUnits) {
-        const int rg = u / (D / 8);
-        const int col = (u % (D / 8)) * 8;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          // columns col + 2p (low halves) and col + 2p + 1 (high halves)
-          const uint32_t a = reg[i][0][p], b = reg[i][1][p];
-          const uint32_t c = reg[i][2][p], e = reg[i][3][p];
-          u32x2 lo, hi;
-          lo[0] = (a & 0xffffu) | (b << 16);
-          lo[1] = (c & 0xffffu) | (e << 16);
-          hi[0] = (a >> 16) | (b & 0xffff0000u);
-          hi[1] = (c >> 16) | (e & 0xffff0000u);
-          *reinterpret_cast<u32x2*>(lds + (col + 2 * p) * kStride + rg * 4) = lo;
-          *reinterpret_cast<u32x2*>(lds + (col + 2 * p + 1) * kStride + rg * 4) = hi;
-        }
-      }
-    }
-  }
-};
-
-// Fragment reads from staged tiles.
-// A/B operand from a natural tile: row `row`, eight consecutive columns at col.
-__device__ __forceinline__ bf16x8 lds_row8(const uint16_t* lds, int stride, int row, int col) {
-  return as_bf16x8(*reinterpret_cast<const u32x4*>(lds + row * stride + col));
+// Operand read, contraction over the tile's columns: row `row`, logical chunk
+// `chunk` (eight consecutive columns) -> bf16x8.
+template <class T>
+__device__ __forceinline__ bf16x8 lds_row_operand(const char* lds, int row, int chunk) {
+  return as_bf16x8(*reinterpret_cast<const u32x4*>(lds + T::off(row, chunk)));
 }
 
-// A/B operand from a transposed tile over the contraction index: row `row`
-// (the free index), contraction positions c0..c0+3 and c1..c1+3.
-__device__ __forceinline__ bf16x8 lds_tr8(const uint16_t* lds, int stride, int row, int c0,
-                                          int c1) {
-  const u32x2 lo = *reinterpret_cast<const u32x2*>(lds + row * stride + c0);
-  const u32x2 hi = *reinterpret_cast<const u32x2*>(lds + row * stride + c1);
-  return bf16x8_from_halves(lo, hi);
+// Transposed operand read, contraction over the tile's rows.  Returns, for
+// lane l (r = l % 32, g = l / 32), the eight values
+//   tile[k0 + (j/4)*8 + g*4 + j%4][col0 + r],  j = 0..7
+// which is the A operand whose (g, j) -> k order matches a C fragment's
+// registers 8s..8s+7 (rows (2s + j/4)*8 + g*4 + j%4 of the C block, with
+// k0 = 16 s + block offset).  Uses ds_read_b64_tr_b16: within each 16-lane
+// group, lane i receives element i%4 of the 8-byte pieces addressed by lanes
+// 4e + i/4 (e = 0..3), so lanes addressing rows k0+4g+(s/4), columns
+// col0 + 16*((l/16)%2) + 4*(s%4) (s = l % 16) deliver a 4 x 16 transpose.
+template <class T>
+__device__ __forceinline__ int tr_offset(int k0, int col0, int lane, int half) {
+  const int s = lane & 15, gi = (lane >> 4) & 1, g = lane >> 5;
+  const int row = k0 + half * 8 + g * 4 + (s >> 2);
+  const int col = col0 + 16 * gi + 4 * (s & 3);
+  return T::off(row, col >> 3) + ((col & 7) << 1);
+}
+
+__device__ __forceinline__ u32x2 lds_tr_b64(const char* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
 }
 
 // Block index -> (query/key block, batch*head).  Consecutive block ids are
