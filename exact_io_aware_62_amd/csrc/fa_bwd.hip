@@ -81,7 +81,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const BlockCoord bc = block_coord(p.BH);
+  const BlockCoord bc = block_coord(p.nkb);
   const int kb = bc.blk;
   const int N = p.N;
   const size_t head = (size_t)bc.bh * N * D;
@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   const int nqt = (N + BQ - 1) / BQ;
   const int t_begin = CAUSAL ? (kb * BKB) / BQ : 0;
   const int mcol = SPARSE ? (kb * BKB) / p.mask_block : 0;
-  auto next_tile = [&](int t) -> int {
+  auto next_tile = [&](int t) FA_INLINE -> int {
     if constexpr (SPARSE) {
       while (t < nqt && p.blockmask[(size_t)((t * BQ) / p.mask_block) * p.nbm + mcol] == 0) ++t;
     }
@@ -120,10 +120,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   const float c = p.scale_log2;
 
   float rowv = 0.f;   // thread tid < 2*BQ carries one lse2 / D value of the next tile
-  auto issue = [&](int t, int bufi) {
+  const auto lofs = T::template lane_offsets<NW>(wave, lane);
+  auto issue = [&](int t, int bufi) FA_INLINE {
     char* st = lds + bufi * STAGE;
-    T::template copy<NW>(Qh, t * BQ, N, st + OFF_Q, wave, lane);
-    T::template copy<NW>(dOh, t * BQ, N, st + OFF_O, wave, lane);
+    T::template copy<NW>(Qh, t * BQ, N, st + OFF_Q, wave, lofs);
+    T::template copy<NW>(dOh, t * BQ, N, st + OFF_O, wave, lofs);
     if (tid < 2 * BQ) {
       const int q = t * BQ + (tid % BQ);
       if (tid < BQ)
@@ -132,11 +133,11 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
         rowv = q < N ? Dh[q] : 0.f;
     }
   };
-  auto finish_issue = [&](int bufi) {
+  auto finish_issue = [&](int bufi) FA_INLINE {
     if (tid < 2 * BQ) reinterpret_cast<float*>(lds + bufi * STAGE + OFF_ROW)[tid] = rowv;
   };
 
-  auto compute = [&](auto bufc, int t) {
+  auto compute = [&](auto bufc, int t) FA_INLINE {
     constexpr int BUFI = decltype(bufc)::value;
     const char* st = lds + BUFI * STAGE;
     const char* qt = st + OFF_Q;
@@ -151,14 +152,16 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
     for (int qb2 = 0; qb2 < NQB; ++qb2) {
       s[qb2] = zero16();
       dp[qb2] = zero16();
+    }
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int qb2 = 0; qb2 < NQB; ++qb2) {
         s[qb2] = mfma32x32x16(lds_row_operand<T>(qt + qb2 * 32 * RB, r, 2 * kk + g), kf[kk],
                               s[qb2]);
         dp[qb2] = mfma32x32x16(lds_row_operand<T>(ot + qb2 * 32 * RB, r, 2 * kk + g), vf[kk],
                                dp[qb2]);
       }
-    }
     const bool need_mask = (CAUSAL && q0 < kw + 31) || (q0 + BQ > N) || (kw + 32 > N);
     // P = exp2(S * c - lse2[q]);  dS = P * (dP - D[q])
 #pragma unroll
@@ -265,7 +268,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const BlockCoord bc = block_coord(p.BH);
+  const BlockCoord bc = block_coord(p.nqb);
   const int qb = CAUSAL ? (p.nqb - 1 - bc.blk) : bc.blk;
   const int N = p.N;
   const size_t head = (size_t)bc.bh * N * D;
@@ -287,7 +290,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   const int kend = CAUSAL ? min(N, (qb + 1) * BQ) : N;
   const int ntiles = (kend + BK - 1) / BK;
   const int mrow = SPARSE ? (qb * BQ) / p.mask_block : 0;
-  auto next_tile = [&](int t) -> int {
+  auto next_tile = [&](int t) FA_INLINE -> int {
     if constexpr (SPARSE) {
       const uint8_t* mr = p.blockmask + (size_t)mrow * p.nbm;
       while (t < ntiles && mr[(t * BK) / p.mask_block] == 0) ++t;
@@ -300,13 +303,14 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   for (int db = 0; db < NDB; ++db) dq[db] = zero16();
   const float c = p.scale_log2;
 
-  auto issue = [&](int t, int bufi) {
+  const auto lofs = T::template lane_offsets<NW>(wave, lane);
+  auto issue = [&](int t, int bufi) FA_INLINE {
     char* st = lds + bufi * STAGE;
-    T::template copy<NW>(Kh, t * BK, N, st, wave, lane);
-    T::template copy<NW>(Vh, t * BK, N, st + T::kBytes, wave, lane);
+    T::template copy<NW>(Kh, t * BK, N, st, wave, lofs);
+    T::template copy<NW>(Vh, t * BK, N, st + T::kBytes, wave, lofs);
   };
 
-  auto compute = [&](auto bufc, int t) {
+  auto compute = [&](auto bufc, int t) FA_INLINE {
     constexpr int BUFI = decltype(bufc)::value;
     const char* kt = lds + BUFI * STAGE;
     const char* vt = kt + T::kBytes;
@@ -317,13 +321,15 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     for (int kb = 0; kb < 2; ++kb) {
       s[kb] = zero16();
       dp[kb] = zero16();
+    }
 #pragma unroll
-      for (int kk = 0; kk < NKK; ++kk) {
+    for (int kk = 0; kk < NKK; ++kk)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
         s[kb] = mfma32x32x16(lds_row_operand<T>(kt + kb * 32 * RB, r, 2 * kk + g), qf[kk], s[kb]);
         dp[kb] = mfma32x32x16(lds_row_operand<T>(vt + kb * 32 * RB, r, 2 * kk + g), of[kk],
                               dp[kb]);
       }
-    }
     const bool need_mask = (CAUSAL && k0 + BK - 1 > q0w) || (k0 + BK > N);
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)

@@ -19,6 +19,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+// Lambdas that capture by reference must be inlined: an out-of-line call
+// would place every captured variable in scratch memory.
+#define FA_INLINE __attribute__((always_inline))
+
 namespace fa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -32,6 +36,10 @@ typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr float kLog2e = 1.4426950408889634f;
+// Word 3 of a raw buffer resource on gfx9-family GPUs: 32-bit data format,
+// no swizzle; the range check then compares each lane's byte offset with
+// the resource's num_records.
+constexpr int kBufferWord3 = 0x00020000;
 constexpr float kLn2 = 0.6931471805599453f;
 // Finite stand-in for "no score seen yet" in the running maximum: keeps
 // exp2(m_old - m_new) and exp2(-inf - m) free of inf - inf.
@@ -85,6 +93,14 @@ __device__ __forceinline__ u32x2 pack_bf16x4(float a0, float a1, float a2, float
   return __builtin_bit_cast(u32x2, r);
 }
 
+// This lane's index in its wavefront, recomputed where it is used (two
+// vector ops; asm so the compiler neither hoists nor keeps it in a register).
+__device__ __forceinline__ int lane_id() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // max over lanes l and l ^ 32 (the two halves of a wavefront), without LDS:
@@ -113,6 +129,12 @@ __device__ __forceinline__ u32x4 zero_u32x4() {
 }
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Per-lane byte offsets of a tile copy, one per copy segment of a wavefront.
+template <int NSEG>
+struct LaneOffsets {
+  int v[NSEG];
+};
 
 // ---------------------------------------------------------------------------
 // LDS tile: ROWS x D bf16 (one head, consecutive tokens), row-major with no
@@ -145,23 +167,41 @@ struct LdsTile {
     return row * kRowBytes + ((chunk ^ swz(row)) << 4);
   }
 
-  // The NW wavefronts of a workgroup copy rows [row0, row0 + ROWS) of `src`
-  // (row stride D) into `lds`.  Asynchronous: wait_vmem() + a barrier before
-  // the data is read.
+  // Per-lane part of the copy: byte offset of the 16 bytes that lane `lane`
+  // of wavefront `wave` fetches for copy segment i, relative to the tile's
+  // first row.  Loop-invariant, so a kernel computes it once.
   template <int NW>
-  __device__ static __forceinline__ void copy(const uint16_t* __restrict__ src, int row0,
-                                              int n_valid, char* lds, int wave, int lane) {
+  __device__ static __forceinline__ LaneOffsets<kSegs / NW> lane_offsets(int wave, int lane) {
     static_assert(kSegs % NW == 0, "segments per wavefront");
+    LaneOffsets<kSegs / NW> o;
 #pragma unroll
     for (int i = 0; i < kSegs / NW; ++i) {
-      const int seg = wave + i * NW;
-      const int P = seg * 64 + lane;
+      const int P = (wave + i * NW) * 64 + lane;
       const int row = P / kCPR;
-      const int chunk = (P % kCPR) ^ swz(row);
-      const int grow = min(row0 + row, n_valid - 1);
-      const uint16_t* g = src + (size_t)grow * D + chunk * 8;
-      __builtin_amdgcn_global_load_lds(g, (lds_void*)(lds + seg * 1024), 16, 0, 0);
+      o.v[i] = row * kRowBytes + (((P % kCPR) ^ swz(row)) << 4);
     }
+    return o;
+  }
+
+  // The NW wavefronts of a workgroup copy rows [row0, row0 + ROWS) of `src`
+  // (row stride D, rows valid below n_valid) into `lds`, with buffer loads
+  // that write LDS directly.  The buffer resource spans only the valid rows
+  // of the tile, so the hardware range check turns rows at or past n_valid
+  // into zeros (finite values; every kernel masks those rows).  Asynchronous:
+  // wait_vmem() + a barrier before the data is read.
+  template <int NW>
+  __device__ static __forceinline__ void copy(const uint16_t* __restrict__ src, int row0,
+                                              int n_valid, char* lds, int wave,
+                                              const LaneOffsets<kSegs / NW>& o) {
+#if defined(__HIP_DEVICE_COMPILE__)   // the buffer builtins exist only for the GPU target
+    const int rows = min(n_valid - row0, ROWS);
+    const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(src + (size_t)row0 * D), (short)0, rows * kRowBytes, kBufferWord3);
+#pragma unroll
+    for (int i = 0; i < kSegs / NW; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_void*)(lds + (wave + i * NW) * 1024),
+                                               16, o.v[i], 0, 0, 0);
+#endif
   }
 };
 
@@ -194,19 +234,65 @@ __device__ __forceinline__ u32x2 lds_tr_b64(const char* p) {
   return __builtin_bit_cast(u32x2, v);
 }
 
-// Block index -> (query/key block, batch*head).  Consecutive block ids are
-// spread round-robin over the 8 XCDs, so with bid = blk * BH + bh every
-// block of one head lands on the same XCD (bh % 8) whenever BH % 8 == 0 and
-// they share that XCD's L2 for K and V.
+// (a ^ b) + c in one v_xad_u32.  Written as asm so that loop-invariant
+// address arithmetic is recomputed where it is used instead of being hoisted
+// into long-lived registers (which a kernel near its register limit would
+// spill, and a spill reload waits for every earlier vector-memory load).
+__device__ __forceinline__ int xad(int a, int b, int c) {
+  int d;
+  asm volatile("v_xad_u32 %0, %1, %2, %3" : "=v"(d) : "v"(a), "s"(b), "v"(c));
+  return d;
+}
+
+// Lane-dependent parts of the two operand reads of a swizzled tile T, such
+// that (with k-step kk and 32-column block db of the tile):
+//   row read  lds_row_operand<T>(base, r, 2*kk + g) == base + xad(xr, kk << 5, ar)
+//   tr read   tr_offset<T>(0, db*32, lane, half)    == xad(xt, db << 6, at[half])
+// The XOR swizzle only permutes chunks inside a row, and its bits above the
+// two lowest chunk bits do not depend on the tr-read half, which is what
+// makes both forms exact (checked against the direct formulas on the host).
+template <class T>
+struct OperandAddr {
+  int ar, xr;        // row read
+  int at0, at1, xt;  // transposed read, halves 0 and 1
+};
+
+template <class T>
+__device__ __forceinline__ OperandAddr<T> operand_addr(int lane) {
+  OperandAddr<T> o;
+  const int r = lane & 31, g = lane >> 5;
+  o.ar = r * T::kRowBytes;
+  o.xr = (g ^ T::swz(r)) << 4;
+  const int s = lane & 15, gi = (lane >> 4) & 1;
+  const int lo = 2 * gi + ((s & 3) >> 1);
+  int at[2], xt = 0;
+#pragma unroll
+  for (int half = 0; half < 2; ++half) {
+    const int row = half * 8 + g * 4 + (s >> 2);
+    const int sw = T::swz(row);
+    at[half] = row * T::kRowBytes + ((lo ^ (sw & 3)) << 4) + ((s & 1) << 3);
+    xt = (sw & ~3) << 4;
+  }
+  o.at0 = at[0];
+  o.at1 = at[1];
+  o.xt = xt;
+  return o;
+}
+
+// Block index -> (query/key block, batch*head), block-major: the first BH ids
+// take block 0 of every head, the next BH block 1, and so on.  Kernels that
+// reverse the block order under a causal mask thereby launch the longest
+// blocks of every head first, which keeps the end of the grid short.
 struct BlockCoord {
   int blk;
   int bh;
 };
 
-__device__ __forceinline__ BlockCoord block_coord(int BH) {
+__device__ __forceinline__ BlockCoord block_coord(int nblk) {
+  const int BH = (int)gridDim.x / nblk;
   BlockCoord c;
-  c.bh = blockIdx.x % BH;
-  c.blk = blockIdx.x / BH;
+  c.blk = (int)blockIdx.x / BH;
+  c.bh = (int)blockIdx.x - c.blk * BH;
   return c;
 }
 

@@ -13,8 +13,8 @@
 //
 // Work split (gfx950): a workgroup is 4 wavefronts and 128 query rows; each
 // wavefront owns 32 rows, held in registers.  Key/value tiles of 64 rows are
-// copied HBM -> LDS asynchronously (global_load_lds), double-buffered: the
-// copy of tile t+1 is in flight while tile t is multiplied.
+// copied HBM -> LDS asynchronously (global_load_lds), K and V each
+// double-buffered.
 //
 // The scores are computed transposed, S^T = K Q^T, on the 32x32x16 bf16
 // matrix cores, so that every lane holds one query row (lanes r and r + 32
@@ -22,6 +22,19 @@
 // work plus one exchange between the two lane halves.  The probabilities
 // stay in registers and feed O^T += V^T P^T as the B operand directly; the
 // V^T operand is read from the natural V tile with the LDS transpose read.
+//
+// Software pipeline.  A matrix-core op runs for 32 cycles, during which the
+// same wavefront can issue independent vector ops; the exp2 work of the
+// softmax (about half the matrix time at d = 128) therefore hides behind
+// matrix work only if the two are interleaved in one instruction stream.
+// Iteration i holds the scores S_i of tile i (computed in iteration i-1):
+//   phase 1  mask S_i if the tile needs it, row max, rare rescale of O;
+//   phase 2  S_{i+1} = K_{i+1} Q^T on the matrix cores, interleaved with
+//            P_i = exp2(S_i c - m) and its bf16 packing;
+//   phase 3  O^T += V_i^T P_i^T, interleaved with the row sum of P_i and
+//            the row max of S_{i+1}.
+// Masked tiles (causal diagonal, ragged end) are always the last tiles of
+// a row block, so masking stays in phase 1 outside the interleaved code.
 
 #include <type_traits>
 
@@ -33,17 +46,25 @@ namespace fa {
 template <int D, bool CAUSAL, bool SPARSE>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   constexpr int BQ = 128, BK = 64, NW = 4;
+  constexpr float kSlack = 8.0f;
   constexpr int NDB = D / 32;   // 32-wide column blocks of O^T
   constexpr int NKK = D / 16;   // k-steps over the head dimension
   using T = LdsTile<BK, D>;
   constexpr int RB = T::kRowBytes;
-  constexpr int STAGE = 2 * T::kBytes;   // K tile, then V tile
-  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+  constexpr int TB = T::kBytes;
+  // K tiles in kbuf0/kbuf1, V tiles in vbuf0/vbuf1.  Four separate arrays,
+  // not one: the compiler can then tell that a read of one buffer does not
+  // touch the buffer an outstanding LDS-DMA copy is filling, and does not
+  // make the read wait for that copy.
+  __shared__ __attribute__((aligned(1024))) char kbuf0[TB];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[TB];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[TB];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[TB];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const BlockCoord bc = block_coord(p.BH);
+  const BlockCoord bc = block_coord(p.nqb);
   // heaviest query blocks first under the causal mask
   const int qb = CAUSAL ? (p.nqb - 1 - bc.blk) : bc.blk;
   const int N = p.N;
@@ -66,12 +87,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const int kend = CAUSAL ? min(N, (qb + 1) * BQ) : N;
   const int ntiles = (kend + BK - 1) / BK;
   const int mrow = SPARSE ? (qb * BQ) / p.mask_block : 0;
-  auto next_tile = [&](int t) -> int {
+  auto next_tile = [&](int t) FA_INLINE -> int {
     if constexpr (SPARSE) {
       const uint8_t* mr = p.blockmask + (size_t)mrow * p.nbm;
       while (t < ntiles && mr[(t * BK) / p.mask_block] == 0) ++t;
     }
     return t;
+  };
+  // wavefront-uniform tile predicates
+  auto needs_mask = [&](int t) FA_INLINE {
+    return (CAUSAL && t * BK + BK - 1 > q0w) || (t * BK + BK > N);
   };
 
   f32x16 oacc[NDB];
@@ -81,97 +106,220 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   float l_run = 0.f;       // running partial row sum (this lane's keys)
   const float c = p.scale_log2;
 
-  auto issue = [&](int t, int bufi) {
-    char* st = lds + bufi * STAGE;
-    T::template copy<NW>(Kh, t * BK, N, st, wave, lane);
-    T::template copy<NW>(Vh, t * BK, N, st + T::kBytes, wave, lane);
+  const auto lofs = T::template lane_offsets<NW>(wave, lane);
+  auto load_k = [&](int t, int buf) FA_INLINE {
+    T::template copy<NW>(Kh, t * BK, N, buf ? kbuf1 : kbuf0, wave, lofs);
+  };
+  auto load_v = [&](int t, int buf) FA_INLINE {
+    T::template copy<NW>(Vh, t * BK, N, buf ? vbuf1 : vbuf0, wave, lofs);
   };
 
-  auto compute = [&](auto bufc, int t) {
-    constexpr int BUFI = decltype(bufc)::value;
-    const char* kt = lds + BUFI * STAGE;
-    const char* vt = kt + T::kBytes;
-    const int k0 = t * BK;
-    // this wavefront skips tiles that lie entirely above its diagonal
-    if (CAUSAL && k0 > q0w + 31) return;
-    // S^T (64 keys x 32 queries) as two 32x32 blocks
-    f32x16 s[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = zero16();
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        s[kb] = mfma32x32x16(lds_row_operand<T>(kt + kb * 32 * RB, r, 2 * kk + g), qf[kk],
-                             s[kb]);
-    }
-    // mask: causal diagonal tile, or keys past the end of the sequence
-    if ((CAUSAL && k0 + BK - 1 > q0w) || k0 + BK > N) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-          if (key >= N || (CAUSAL && key > qrow)) s[kb][i] = -INFINITY;
-        }
-    }
-    // online softmax update
+  auto rowmax = [&](const f32x16 (&s)[2]) {
     float mx = s[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    mx = max_xor32(mx);
-    const float m_new = fmaxf(m_run, mx * c);
-    const float alpha = exp2_fast(m_run - m_new);
-    m_run = m_new;
-    float rs = 0.f;
+    return mx;
+  };
+  // P = exp2(S c - m), packed to the bf16 B operands of the PV product:
+  // k-step ks2 of key block kb uses C registers 8*ks2 .. 8*ks2+7.
+  auto exponentiate = [&](f32x16 (&s)[2], bf16x8 (&pb)[4]) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float e = exp2_fast(__builtin_fmaf(s[kb][i], c, -m_new));
-        s[kb][i] = e;
-        rs += e;
+      for (int i = 0; i < 16; ++i) s[kb][i] = exp2_fast(__builtin_fmaf(s[kb][i], c, -m_run));
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) pb[kb * 2 + ks2] = pack_c8(s[kb], 8 * ks2);
+  };
+  auto rowsum = [&](const f32x16 (&s)[2]) {
+    float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; i += 4) {
+        a0 += s[kb][i];
+        a1 += s[kb][i + 1];
+        a2 += s[kb][i + 2];
+        a3 += s[kb][i + 3];
       }
-    l_run = l_run * alpha + rs;
-    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+    return (a0 + a1) + (a2 + a3);
+  };
+  f32x16 sc[2];          // scores of the current tile
+  // bf16 probabilities: phase B reads entry q for the previous tile's P V
+  // product and then overwrites it with the current tile's packed P.
+  bf16x8 pb[4];
+
+  // row max over this lane's scores (raw units)
+  // phase 1 for tile tc: mask, row max, move the running max if needed.
+  // Returns the factor the accumulated O must be scaled by (1 if unmoved).
+  auto phase1 = [&](int tc) FA_INLINE -> float {
+    if (needs_mask(tc)) {
+      // register i of key block kb holds key k0 + g*4 + kb*32 + (i/4)*8 + i%4;
+      // compare the constant part against one per-lane bound
+      // lane id recomputed here (two vector ops) rather than kept live
+      const int ln = lane_id();
+      const int kl = tc * BK + (ln >> 5) * 4;
+      const int lim = CAUSAL ? min(N - 1, q0w + (ln & 31)) - kl : N - 1 - kl;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) sc[kb][i] = -INFINITY;
+    }
+    // The running maximum only moves when a score exceeds it by more than
+    // kSlack (log2 units): every exp2 argument then stays below kSlack, far
+    // inside fp32 and bf16 range, and since the final 1/l and LSE use the
+    // same m the result is the same for any such m.  With scores of a few
+    // units this rescales O about once per row.
+    const float mxc = max_xor32(rowmax(sc)) * c;
+    float alpha = 1.f;
+    if (mxc > m_run + kSlack) {
+      alpha = exp2_fast(m_run - mxc);
+      m_run = mxc;
+      l_run *= alpha;
+    }
+    return alpha;
+  };
+
+  const OperandAddr<T> oa = operand_addr<T>(lane);
+  // V^T operand for product j of the PV step: key block kb = j / (2 NDB),
+  // k-step ks2 = (j / NDB) % 2, output column block db = j % NDB.  The
+  // lane-dependent offsets are loop-invariant; with compile-time buffers
+  // the compiler keeps them in registers and folds the rest into the
+  // instruction's immediate offset.
+  auto vread = [&](const char* vt, int j) FA_INLINE {
+    const int kb = j / (2 * NDB), ks2 = (j / NDB) & 1, db = j % NDB;
+    const char* vk = vt + (kb * 32 + 16 * ks2) * RB + (oa.xt ^ (db << 6));
+    return bf16x8_from_halves(lds_tr_b64(vk + oa.at0), lds_tr_b64(vk + oa.at1));
+  };
+  // phase B: O += P_prev V_prev on the matrix cores, interleaved with
+  // P = exp2(S c - m) of the current tile, its bf16 packing and row sum.
+  // Program order is the issue order (each step is fenced): V^T fragments
+  // are read PF products ahead, the vector work is spread evenly.
+  auto phaseB = [&](const char* vt) FA_INLINE {
+    constexpr int NJ = 4 * NDB, PF = 2;
+    bf16x8 vfr[NJ];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < PF; ++j) vfr[j] = vread(vt, j);
+    float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int kb = j / (2 * NDB), ks2 = (j / NDB) & 1, db = j % NDB;
+      oacc[db] = mfma32x32x16(vfr[j], pb[kb * 2 + ks2], oacc[db]);
+      if (j + PF < NJ) vfr[j + PF] = vread(vt, j + PF);
+      // P entry q = j / NDB is last read by product j = NDB q + NDB - 1 and
+      // is repacked right after it (exps 8q .. 8q+7 fall in those steps)
+#pragma unroll
+      for (int e = j * 32 / NJ; e < (j + 1) * 32 / NJ; ++e) {
+        const int b = e >> 4, i = e & 15;
+        // the row sum is taken over the fp32 probabilities: a sum of the
+        // bf16-rounded ones would move LSE by up to 2^-9 on short rows
+        const float pe = exp2_fast(__builtin_fmaf(sc[b][i], c, -m_run));
+        sc[b][i] = pe;
+        if (e & 1) a1 += pe; else a0 += pe;
+        if ((i & 7) == 7) pb[b * 2 + (i >> 3)] = pack_c8(sc[b], i - 7);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return a0 + a1;
+  };
+  // O += P V alone (the last product of a wavefront), same issue order
+  auto pv_only = [&](const char* vt) FA_INLINE {
+    constexpr int NJ = 4 * NDB, PF = 2;
+    bf16x8 vfr[NJ];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < PF; ++j) vfr[j] = vread(vt, j);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      const int kb = j / (2 * NDB), ks2 = (j / NDB) & 1, db = j % NDB;
+      oacc[db] = mfma32x32x16(vfr[j], pb[kb * 2 + ks2], oacc[db]);
+      if (j + PF < NJ) vfr[j + PF] = vread(vt, j + PF);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  // scores of the tile in K buffer kt (phase A); K fragments read PF ahead
+  auto phaseA = [&](const char* kt) FA_INLINE {
+    // product j: k-step kk = j / 2 of key block kb = j % 2 (two independent
+    // accumulation chains); one address per k-step serves both blocks
+    constexpr int NJ = 2 * NKK, PF = 4;
+    bf16x8 kfr[NJ];
+    auto kread = [&](int j) FA_INLINE {
+      const char* a = kt + (j & 1) * 32 * RB + (oa.xr ^ ((j >> 1) << 5)) + oa.ar;
+      kfr[j] = as_bf16x8(*reinterpret_cast<const u32x4*>(a));
+    };
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < PF; ++j) kread(j);
+    sc[0] = zero16();
+    sc[1] = zero16();
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      sc[j & 1] = mfma32x32x16(kfr[j], qf[j >> 1], sc[j & 1]);
+      if (j + PF < NJ) kread(j + PF);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  auto rescale = [&](float alpha) FA_INLINE {
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
       for (int db = 0; db < NDB; ++db)
 #pragma unroll
         for (int i = 0; i < 16; ++i) oacc[db][i] *= alpha;
     }
-    // O^T += V^T P^T; k-step ks2 of key block kb uses C registers 8*ks2..+7
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        const bf16x8 pb = pack_c8(s[kb], 8 * ks2);
-        const char* vk = vt + (kb * 32 + 16 * ks2) * RB;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const bf16x8 a = bf16x8_from_halves(lds_tr_b64(vk + tr_offset<T>(0, db * 32, lane, 0)),
-                                              lds_tr_b64(vk + tr_offset<T>(0, db * 32, lane, 1)));
-          oacc[db] = mfma32x32x16(a, pb, oacc[db]);
-        }
-      }
   };
 
-  int t = next_tile(0);
-  if (t < ntiles) issue(t, 0);
-  while (t < ntiles) {
+  // One iteration for tile tc, whose K is in K buffer PAR; the previous
+  // tile's V is in V buffer 1 - PAR and its probabilities in pb.  FIRST:
+  // there is no previous tile (O is still zero).
+  auto iteration = [&](auto parc, auto firstc, int& tc, int& tn) FA_INLINE {
+    constexpr int PAR = decltype(parc)::value;
+    constexpr bool FIRST = decltype(firstc)::value;
     wait_vmem();
     __syncthreads();
-    int tn = next_tile(t + 1);
-    if (tn < ntiles) issue(tn, 1);
-    compute(std::integral_constant<int, 0>{}, t);
-    t = tn;
-    if (t >= ntiles) break;
+    const int tn2 = tn < ntiles ? next_tile(tn + 1) : ntiles;
+    if (tn < ntiles) load_k(tn, 1 - PAR);
+    load_v(tc, PAR);
+    // A tile entirely above this wavefront's causal diagonal is processed
+    // like any other: the mask sets all its scores to -inf, so its P is 0
+    // and O is unchanged.  One code path keeps O in one register set.
+    phaseA(PAR ? kbuf1 : kbuf0);
+    const float alpha = phase1(tc);
+    if constexpr (FIRST) {
+      exponentiate(sc, pb);
+      l_run += rowsum(sc);
+    } else {
+      l_run += phaseB(PAR ? vbuf0 : vbuf1);
+      rescale(alpha);
+    }
+    tc = tn;
+    tn = tn2;
+  };
+
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  int tc = next_tile(0);
+  int tn = tc < ntiles ? next_tile(tc + 1) : ntiles;
+  if (tc < ntiles) {
+    load_k(tc, 0);
+    iteration(P0{}, std::true_type{}, tc, tn);
+    // whole pairs of tiles: the loop body has one entry and one exit, which
+    // keeps O in one register set across both halves
+    while (tn < ntiles) {
+      iteration(P1{}, std::false_type{}, tc, tn);
+      iteration(P0{}, std::false_type{}, tc, tn);
+    }
+    const bool odd = tc < ntiles;   // one tile left (parity 1)
+    if (odd) iteration(P1{}, std::false_type{}, tc, tn);
+    // the last tile's P V product
     wait_vmem();
     __syncthreads();
-    tn = next_tile(t + 1);
-    if (tn < ntiles) issue(tn, 0);
-    compute(std::integral_constant<int, 1>{}, t);
-    t = tn;
+    if (odd) pv_only(vbuf1);
+    else pv_only(vbuf0);
   }
 
   // epilogue: combine the two lane halves' partial sums, divide once
