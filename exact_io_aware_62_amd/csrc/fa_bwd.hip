@@ -73,10 +73,16 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   constexpr int NDB = D / 32, NKK = D / 16, NQB = BQ / 32;
   using T = LdsTile<BQ, D>;
   constexpr int RB = T::kRowBytes;
-  // per stage: Q tile, dO tile, lse2[BQ] and D[BQ] (padded to 1 KB)
-  constexpr int OFF_Q = 0, OFF_O = T::kBytes, OFF_ROW = 2 * T::kBytes;
-  constexpr int STAGE = 2 * T::kBytes + 1024;
-  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+  // per stage: Q tile, dO tile, lse2[BQ] and D[BQ].  Separate arrays per
+  // tile and stage: the compiler can then tell that a read of one buffer does
+  // not touch the buffer an outstanding LDS-DMA copy is filling, and does not
+  // make the read wait for that copy.
+  __shared__ __attribute__((aligned(1024))) char qbuf0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char qbuf1[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char obuf0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char obuf1[T::kBytes];
+  __shared__ __attribute__((aligned(16))) float rowbuf0[2 * BQ];
+  __shared__ __attribute__((aligned(16))) float rowbuf1[2 * BQ];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
@@ -119,30 +125,37 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   }
   const float c = p.scale_log2;
 
-  float rowv = 0.f;   // thread tid < 2*BQ carries one lse2 / D value of the next tile
+  // Thread tid < 2*BQ carries one LSE / D value of the next tile: it is
+  // loaded before that tile's LDS-DMA copies are issued (vector-memory waits
+  // complete in issue order, so waiting for it then does not wait for the
+  // copies) and converted and stored only after the current tile's compute.
+  float rowv = 0.f;
+  int rowq = 0;
   const auto lofs = T::template lane_offsets<NW>(wave, lane);
   auto issue = [&](int t, int bufi) FA_INLINE {
-    char* st = lds + bufi * STAGE;
-    T::template copy<NW>(Qh, t * BQ, N, st + OFF_Q, wave, lofs);
-    T::template copy<NW>(dOh, t * BQ, N, st + OFF_O, wave, lofs);
     if (tid < 2 * BQ) {
-      const int q = t * BQ + (tid % BQ);
-      if (tid < BQ)
-        rowv = q < N ? lse_to_log2(lseh[q]) : INFINITY;
-      else
-        rowv = q < N ? Dh[q] : 0.f;
+      rowq = t * BQ + (tid % BQ);
+      const int qc = min(rowq, N - 1);
+      rowv = tid < BQ ? lseh[qc] : Dh[qc];
     }
+    T::template copy<NW>(Qh, t * BQ, N, bufi ? qbuf1 : qbuf0, wave, lofs);
+    T::template copy<NW>(dOh, t * BQ, N, bufi ? obuf1 : obuf0, wave, lofs);
   };
   auto finish_issue = [&](int bufi) FA_INLINE {
-    if (tid < 2 * BQ) reinterpret_cast<float*>(lds + bufi * STAGE + OFF_ROW)[tid] = rowv;
+    __builtin_amdgcn_sched_barrier(0);
+    if (tid < 2 * BQ) {
+      float v;
+      if (tid < BQ) v = rowq < N ? lse_to_log2(rowv) : INFINITY;
+      else v = rowq < N ? rowv : 0.f;
+      (bufi ? rowbuf1 : rowbuf0)[tid] = v;
+    }
   };
 
   auto compute = [&](auto bufc, int t) FA_INLINE {
     constexpr int BUFI = decltype(bufc)::value;
-    const char* st = lds + BUFI * STAGE;
-    const char* qt = st + OFF_Q;
-    const char* ot = st + OFF_O;
-    const float* lse2 = reinterpret_cast<const float*>(st + OFF_ROW);
+    const char* qt = BUFI ? qbuf1 : qbuf0;
+    const char* ot = BUFI ? obuf1 : obuf0;
+    const float* lse2 = BUFI ? rowbuf1 : rowbuf0;
     const float* dsum = lse2 + BQ;
     const int q0 = t * BQ;
     if (CAUSAL && q0 + BQ - 1 < kw) return;   // every query of the tile precedes our keys
@@ -262,8 +275,11 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   constexpr int NDB = D / 32, NKK = D / 16;
   using T = LdsTile<BK, D>;
   constexpr int RB = T::kRowBytes;
-  constexpr int STAGE = 2 * T::kBytes;   // K tile, then V tile
-  __shared__ __attribute__((aligned(1024))) char lds[2 * STAGE];
+  // K and V tiles, two stages, in separate arrays (see dkdv_kernel)
+  __shared__ __attribute__((aligned(1024))) char kbuf0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char kbuf1[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char vbuf0[T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char vbuf1[T::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
@@ -305,15 +321,14 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
 
   const auto lofs = T::template lane_offsets<NW>(wave, lane);
   auto issue = [&](int t, int bufi) FA_INLINE {
-    char* st = lds + bufi * STAGE;
-    T::template copy<NW>(Kh, t * BK, N, st, wave, lofs);
-    T::template copy<NW>(Vh, t * BK, N, st + T::kBytes, wave, lofs);
+    T::template copy<NW>(Kh, t * BK, N, bufi ? kbuf1 : kbuf0, wave, lofs);
+    T::template copy<NW>(Vh, t * BK, N, bufi ? vbuf1 : vbuf0, wave, lofs);
   };
 
   auto compute = [&](auto bufc, int t) FA_INLINE {
     constexpr int BUFI = decltype(bufc)::value;
-    const char* kt = lds + BUFI * STAGE;
-    const char* vt = kt + T::kBytes;
+    const char* kt = BUFI ? kbuf1 : kbuf0;
+    const char* vt = BUFI ? vbuf1 : vbuf0;
     const int k0 = t * BK;
     if (CAUSAL && k0 > q0w + 31) return;
     f32x16 s[2], dp[2];
