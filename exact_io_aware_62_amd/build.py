@@ -28,6 +28,8 @@ COMMON_FLAGS = [
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE, "-I", CSRC,
 ]
+# Per-source extra flags (none at present).
+SOURCE_FLAGS: dict = {}
 
 
 def hipcc() -> str:
@@ -47,7 +49,8 @@ def build_library(verbose: bool = False, extra_flags: list[str] | None = None) -
     for src in SOURCES:
         obj = os.path.join(OBJDIR, os.path.splitext(src)[0] + ".o")
         lang = ["-x", "hip"] if src.endswith(".hip") else []
-        cmd = [cc, *flags, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [cc, *flags, *SOURCE_FLAGS.get(src, []), *lang, "-c", os.path.join(CSRC, src), "-o",
+               obj]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((src, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT,

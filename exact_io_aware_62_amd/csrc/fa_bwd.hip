@@ -59,30 +59,31 @@ __global__ __launch_bounds__(256) void dsum_kernel(BwdParams p, long long rows) 
 
 // ---------------------------------------------------------------------------
 // 2. dK, dV.  Workgroup = 4 wavefronts = 128 keys; wavefront w owns keys
-//    kw .. kw+31 and keeps K and V rows for them in registers.  Query tiles
-//    of 64 rows (Q and dO, natural layout) are copied HBM -> LDS
-//    asynchronously, double-buffered.  S = Q K^T and dP = dO V^T contract
-//    over d (row operands); dV^T += dO^T P and dK^T += Q^T dS contract over
-//    queries, with dO^T and Q^T read by the LDS transpose read.  Scores are
-//    formed as S (queries x keys) so each lane owns one key and the P / dS
-//    fragments feed the dV / dK products as B operands directly.
+//    kw .. kw+31: their V rows in registers, the workgroup's K rows in LDS
+//    (copied once).  Query tiles of 32 rows (Q and dO, natural layout) are
+//    copied HBM -> LDS asynchronously, double-buffered.  S = Q K^T and
+//    dP = dO V^T contract over d (row operands); dV^T += dO^T P and
+//    dK^T += Q^T dS contract over queries, with dO^T and Q^T read by the LDS
+//    transpose read.  Scores are formed as S (queries x keys) so each lane
+//    owns one key and the P / dS fragments feed the dV / dK products as B
+//    operands directly.  K in LDS and 32-row tiles keep every live value in
+//    at most 256 vector registers (two wavefronts per SIMD, no accumulator
+//    registers), and the LDS footprint lets two workgroups share a CU.
 // ---------------------------------------------------------------------------
 template <int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
-  constexpr int BKB = 128, BQ = 64, NW = 4;
-  constexpr int NDB = D / 32, NKK = D / 16, NQB = BQ / 32;
-  using T = LdsTile<BQ, D>;
-  constexpr int RB = T::kRowBytes;
-  // per stage: Q tile, dO tile, lse2[BQ] and D[BQ].  Separate arrays per
-  // tile and stage: the compiler can then tell that a read of one buffer does
-  // not touch the buffer an outstanding LDS-DMA copy is filling, and does not
-  // make the read wait for that copy.
-  __shared__ __attribute__((aligned(1024))) char qbuf0[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) char qbuf1[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) char obuf0[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) char obuf1[T::kBytes];
-  __shared__ __attribute__((aligned(16))) float rowbuf0[2 * BQ];
-  __shared__ __attribute__((aligned(16))) float rowbuf1[2 * BQ];
+__global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
+  constexpr int BKB = 128, BQ = 32, NW = 4;
+  constexpr int NDB = D / 32, NKK = D / 16;
+  using TQ = LdsTile<BQ, D>;    // a query tile of Q or dO
+  using TK = LdsTile<BKB, D>;   // the workgroup's K rows
+  constexpr int RB = TQ::kRowBytes;
+  // K rows of the workgroup; two stages of the Q and dO tiles and of the
+  // per-query lse2 / D values.  The tiles are filled by copy_async, and the
+  // stage is chosen at run time, so one loop body serves both stages.
+  __shared__ __attribute__((aligned(1024))) char kbuf[TK::kBytes];
+  __shared__ __attribute__((aligned(1024))) char qbuf[2 * TQ::kBytes];
+  __shared__ __attribute__((aligned(1024))) char obuf[2 * TQ::kBytes];
+  __shared__ __attribute__((aligned(16))) float rowbuf[2 * 2 * BQ];   // lse2 then D
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
@@ -98,13 +99,13 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
 
   const int kw = kb * BKB + wave * 32;   // first key of this wavefront
   const int key = kw + r;                // this lane's key
-  bf16x8 kf[NKK], vf[NKK];
+  copy_async<TK, NW>(p.K + head, kb * BKB, N, lds_addr(kbuf), wave,
+                     TK::template lane_offsets<NW>(wave, lane));
+  bf16x8 vf[NKK];
 #pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    const size_t off = (size_t)key * D + kk * 16 + g * 8;
-    kf[kk] = as_bf16x8(key < N ? ldg16(p.K + head + off) : zero_u32x4());
-    vf[kk] = as_bf16x8(key < N ? ldg16(p.V + head + off) : zero_u32x4());
-  }
+  for (int kk = 0; kk < NKK; ++kk)
+    vf[kk] = as_bf16x8(key < N ? ldg16(p.V + head + (size_t)key * D + kk * 16 + g * 8)
+                               : zero_u32x4());
 
   // query tiles: causal => only rows >= first key of the block
   const int nqt = (N + BQ - 1) / BQ;
@@ -113,6 +114,12 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   auto next_tile = [&](int t) FA_INLINE -> int {
     if constexpr (SPARSE) {
       while (t < nqt && p.blockmask[(size_t)((t * BQ) / p.mask_block) * p.nbm + mcol] == 0) ++t;
+    } else {
+      // opaque to the optimizer: with a visible t + 1 sequence it reshapes
+      // the tile loop and the dK / dV accumulators end up copied between
+      // register sets
+      t = __builtin_amdgcn_readfirstlane(t);
+      asm volatile("" : "+s"(t));
     }
     return t;
   };
@@ -131,15 +138,15 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
   // copies) and converted and stored only after the current tile's compute.
   float rowv = 0.f;
   int rowq = 0;
-  const auto lofs = T::template lane_offsets<NW>(wave, lane);
+  const auto lofs = TQ::template lane_offsets<NW>(wave, lane);
   auto issue = [&](int t, int bufi) FA_INLINE {
     if (tid < 2 * BQ) {
       rowq = t * BQ + (tid % BQ);
       const int qc = min(rowq, N - 1);
       rowv = tid < BQ ? lseh[qc] : Dh[qc];
     }
-    T::template copy<NW>(Qh, t * BQ, N, bufi ? qbuf1 : qbuf0, wave, lofs);
-    T::template copy<NW>(dOh, t * BQ, N, bufi ? obuf1 : obuf0, wave, lofs);
+    copy_async<TQ, NW>(Qh, t * BQ, N, lds_addr(qbuf) + bufi * TQ::kBytes, wave, lofs);
+    copy_async<TQ, NW>(dOh, t * BQ, N, lds_addr(obuf) + bufi * TQ::kBytes, wave, lofs);
   };
   auto finish_issue = [&](int bufi) FA_INLINE {
     __builtin_amdgcn_sched_barrier(0);
@@ -147,96 +154,137 @@ __global__ __launch_bounds__(256, 1) void dkdv_kernel(BwdParams p) {
       float v;
       if (tid < BQ) v = rowq < N ? lse_to_log2(rowv) : INFINITY;
       else v = rowq < N ? rowv : 0.f;
-      (bufi ? rowbuf1 : rowbuf0)[tid] = v;
+      rowbuf[bufi * 2 * BQ + tid] = v;
     }
   };
 
-  auto compute = [&](auto bufc, int t) FA_INLINE {
-    constexpr int BUFI = decltype(bufc)::value;
-    const char* qt = BUFI ? qbuf1 : qbuf0;
-    const char* ot = BUFI ? obuf1 : obuf0;
-    const float* lse2 = BUFI ? rowbuf1 : rowbuf0;
+  const OperandAddr<TQ> oa = operand_addr<TQ>(lane);
+  const char* kw_lds = kbuf + wave * 32 * RB;   // this wavefront's K rows
+  // row operand (contraction over d), k-step kk: rows r of `tile`
+  auto row_read = [&](const char* tile, int kk) FA_INLINE {
+    return as_bf16x8(*reinterpret_cast<const u32x4*>(tile + (oa.xr ^ (kk << 5)) + oa.ar));
+  };
+  // transposed operand (contraction over queries) for product j of a dV / dK
+  // step: k-step ks2 = j / NDB (queries 16 ks2 ..), output column block db
+  auto tr_read = [&](const char* tile, int j) FA_INLINE {
+    const int ks2 = j / NDB, db = j % NDB;
+    const char* rk = tile + 16 * ks2 * RB + (oa.xt ^ (db << 6));
+    return bf16x8_from_halves(lds_tr_b64(rk + oa.at0), lds_tr_b64(rk + oa.at1));
+  };
+
+  // One query tile, in four steps of 2 NDB products each; LDS operands are
+  // read ahead and each product is fenced, so issue order = program order:
+  //   1. S = Q K^T               (both operands from LDS)
+  //   2. dP = dO V^T             || P = exp2(S c - lse2), packed to bf16
+  //   3. dV^T += dO^T P          || dS = P (dP - D), packed to bf16
+  //   4. dK^T += Q^T dS
+  auto compute = [&](int stage, int t) FA_INLINE {
+    constexpr int NJ = NKK;   // products per step (= 2 NDB)
+    const char* qt = qbuf + stage * TQ::kBytes;
+    const char* ot = obuf + stage * TQ::kBytes;
+    const float* lse2 = rowbuf + stage * 2 * BQ;
     const float* dsum = lse2 + BQ;
     const int q0 = t * BQ;
-    if (CAUSAL && q0 + BQ - 1 < kw) return;   // every query of the tile precedes our keys
-    // S = Q K^T and dP = dO V^T for NQB blocks of 32 queries
-    f32x16 s[NQB], dp[NQB];
+    f32x16 s, dp;
+    bf16x8 pb[2], sb[2];
+    bf16x8 fa[NJ], fb[NJ];
+    constexpr int PF = 2;
+
+    // 1. S = Q K^T
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int qb2 = 0; qb2 < NQB; ++qb2) {
-      s[qb2] = zero16();
-      dp[qb2] = zero16();
+    for (int j = 0; j < PF; ++j) {
+      fa[j] = row_read(qt, j);
+      fb[j] = row_read(kw_lds, j);
     }
+    s = zero16();
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-      for (int qb2 = 0; qb2 < NQB; ++qb2) {
-        s[qb2] = mfma32x32x16(lds_row_operand<T>(qt + qb2 * 32 * RB, r, 2 * kk + g), kf[kk],
-                              s[qb2]);
-        dp[qb2] = mfma32x32x16(lds_row_operand<T>(ot + qb2 * 32 * RB, r, 2 * kk + g), vf[kk],
-                               dp[qb2]);
+    for (int j = 0; j < NJ; ++j) {
+      s = mfma32x32x16(fa[j], fb[j], s);
+      if (j + PF < NJ) {
+        fa[j + PF] = row_read(qt, j + PF);
+        fb[j + PF] = row_read(kw_lds, j + PF);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // mask: causal diagonal, ragged query or key ends (rare tiles only)
     const bool need_mask = (CAUSAL && q0 < kw + 31) || (q0 + BQ > N) || (kw + 32 > N);
-    // P = exp2(S * c - lse2[q]);  dS = P * (dP - D[q])
+    if (need_mask) {
+      // register i holds query q0 + (i/4)*8 + g*4 + i%4; this lane's key
+      const int ln = lane_id();
+      const int kl = kw + (ln & 31);
+      const int qg = q0 + (ln >> 5) * 4;
 #pragma unroll
-    for (int qb2 = 0; qb2 < NQB; ++qb2)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int ql = qb2 * 32 + i4 * 8 + g * 4;   // local query of register i4*4
-        const f32x4 l4 = *reinterpret_cast<const f32x4*>(lse2 + ql);
-        const f32x4 d4 = *reinterpret_cast<const f32x4*>(dsum + ql);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int i = i4 * 4 + j;
-          float sv = s[qb2][i];
-          if (need_mask) {
-            const int q = q0 + ql + j;
-            if ((CAUSAL && key > q) || q >= N || key >= N) sv = -INFINITY;
-          }
-          const float pv = exp2_fast(__builtin_fmaf(sv, c, -l4[j]));
-          s[qb2][i] = pv;
-          dp[qb2][i] = pv * (dp[qb2][i] - d4[j]);
-        }
+      for (int i = 0; i < 16; ++i) {
+        const int q = qg + (i >> 2) * 8 + (i & 3);
+        if ((CAUSAL && kl > q) || q >= N || kl >= N) s[i] = -INFINITY;
       }
-    // dV^T += dO^T P ;  dK^T += Q^T dS   (contraction over queries)
+    }
+
+    // 2. dP = dO V^T || P
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int qb2 = 0; qb2 < NQB; ++qb2)
+    for (int j = 0; j < PF; ++j) fa[j] = row_read(ot, j);
+    dp = zero16();
 #pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        const bf16x8 pb = pack_c8(s[qb2], 8 * ks2);
-        const bf16x8 sb = pack_c8(dp[qb2], 8 * ks2);
-        const int rb = (qb2 * 32 + 16 * ks2) * RB;
+    for (int j = 0; j < NJ; ++j) {
+      dp = mfma32x32x16(fa[j], vf[j], dp);
+      if (j + PF < NJ) fa[j + PF] = row_read(ot, j + PF);
 #pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const int o0 = tr_offset<T>(0, db * 32, lane, 0), o1 = tr_offset<T>(0, db * 32, lane, 1);
-          const bf16x8 ao = bf16x8_from_halves(lds_tr_b64(ot + rb + o0), lds_tr_b64(ot + rb + o1));
-          dv[db] = mfma32x32x16(ao, pb, dv[db]);
-          const bf16x8 aq = bf16x8_from_halves(lds_tr_b64(qt + rb + o0), lds_tr_b64(qt + rb + o1));
-          dk[db] = mfma32x32x16(aq, sb, dk[db]);
-        }
+      for (int i = j * 16 / NJ; i < (j + 1) * 16 / NJ; ++i) {
+        // LSE (log2 units) of the four queries of registers (i/4)*4 .. +3
+        const float* lq = lse2 + (i >> 2) * 8 + g * 4;
+        s[i] = exp2_fast(__builtin_fmaf(s[i], c, -lq[i & 3]));
+        if ((i & 7) == 7) pb[i >> 3] = pack_c8(s, i - 7);
       }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // 3. dV^T += dO^T P || dS
+#pragma unroll
+    for (int j = 0; j < PF; ++j) fa[j] = tr_read(ot, j);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      dv[j % NDB] = mfma32x32x16(fa[j], pb[j / NDB], dv[j % NDB]);
+      if (j + PF < NJ) fa[j + PF] = tr_read(ot, j + PF);
+#pragma unroll
+      for (int i = j * 16 / NJ; i < (j + 1) * 16 / NJ; ++i) {
+        const float* dq4 = dsum + (i >> 2) * 8 + g * 4;
+        dp[i] = s[i] * (dp[i] - dq4[i & 3]);
+        if ((i & 7) == 7) sb[i >> 3] = pack_c8(dp, i - 7);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // 4. dK^T += Q^T dS
+#pragma unroll
+    for (int j = 0; j < PF; ++j) fa[j] = tr_read(qt, j);
+#pragma unroll
+    for (int j = 0; j < NJ; ++j) {
+      dk[j % NDB] = mfma32x32x16(fa[j], sb[j / NDB], dk[j % NDB]);
+      if (j + PF < NJ) fa[j + PF] = tr_read(qt, j + PF);
+      __builtin_amdgcn_sched_barrier(0);
+    }
   };
 
   int t = next_tile(t_begin);
+  int stage = 0;
   if (t < nqt) {
     issue(t, 0);
     finish_issue(0);
   }
+  // one loop body for both stages keeps the dK / dV accumulators in one
+  // register set
   while (t < nqt) {
     wait_vmem();
     __syncthreads();
-    int tn = next_tile(t + 1);
-    if (tn < nqt) issue(tn, 1);
-    compute(std::integral_constant<int, 0>{}, t);
-    if (tn < nqt) finish_issue(1);
+    const int tn = next_tile(t + 1);
+    if (tn < nqt) issue(tn, stage ^ 1);
+    compute(stage, t);
+    if (tn < nqt) finish_issue(stage ^ 1);
     t = tn;
-    if (t >= nqt) break;
-    wait_vmem();
-    __syncthreads();
-    tn = next_tile(t + 1);
-    if (tn < nqt) issue(tn, 0);
-    compute(std::integral_constant<int, 1>{}, t);
-    if (tn < nqt) finish_issue(0);
-    t = tn;
+    stage ^= 1;
   }
 
   // epilogue: lane owns key `key`; register i of block db is column

@@ -128,7 +128,14 @@ __device__ __forceinline__ u32x4 zero_u32x4() {
   return z;
 }
 
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait for every outstanding vector-memory operation.  The asm form also
+// covers copies issued as asm; the builtin tells the compiler's wait-count
+// tracking that nothing is outstanding any more (vmcnt 0, expcnt and lgkmcnt
+// left at their "don't wait" maxima).
+__device__ __forceinline__ void wait_vmem() {
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
 
 // Per-lane byte offsets of a tile copy, one per copy segment of a wavefront.
 template <int NSEG>
@@ -151,6 +158,8 @@ struct LaneOffsets {
 template <int ROWS, int D>
 struct LdsTile {
   static_assert(D == 64 || D == 128, "head dim");
+  static constexpr int kRows = ROWS;
+  static constexpr int kD = D;
   static constexpr int kCPR = D / 8;                 // chunks per row
   static constexpr int kRowBytes = D * 2;
   static constexpr int kBytes = ROWS * kRowBytes;
@@ -204,6 +213,44 @@ struct LdsTile {
 #endif
   }
 };
+
+// LDS address (32-bit offset in the LDS aperture) of a __shared__ object.
+__device__ __forceinline__ int lds_addr(const void* p) {
+  return (int)(size_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Copy of rows [row0, row0 + ROWS) of `src` into the LDS tile at LDS address
+// `dst` (see LdsTile::copy), issued as asm.  The compiler then sees no LDS
+// write, so it neither makes later LDS reads wait for the copy nor needs to
+// know which buffer a read touches: that lets a kernel pick its LDS stage at
+// run time.  The caller must wait_vmem() and pass a barrier before any
+// wavefront reads the tile (as it has to anyway for the other wavefronts'
+// parts).  M0 is saved and restored around the copies.
+template <class T, int NW>
+__device__ __forceinline__ void copy_async(const uint16_t* __restrict__ src, int row0, int n_valid,
+                                           int dst, int wave, const LaneOffsets<T::kSegs / NW>& o) {
+  const int rows = min(n_valid - row0, T::kRows);
+  const unsigned long long a = (unsigned long long)(src + (size_t)row0 * T::kD);
+  u32x4 rs;
+  rs[0] = __builtin_amdgcn_readfirstlane((unsigned)a);
+  rs[1] = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32) & 0xffffu);   // stride 0
+  rs[2] = __builtin_amdgcn_readfirstlane((unsigned)(rows * T::kRowBytes));
+  rs[3] = (unsigned)kBufferWord3;
+#pragma unroll
+  for (int i = 0; i < T::kSegs / NW; ++i) {
+    const int seg = __builtin_amdgcn_readfirstlane(dst + (wave + i * NW) * 1024);
+    int saved;
+    asm volatile(
+        "s_mov_b32 %0, m0\n\t"
+        "s_mov_b32 m0, %3\n\t"
+        "s_nop 0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds\n\t"
+        "s_mov_b32 m0, %0"
+        : "=&s"(saved)
+        : "v"(o.v[i]), "s"(rs), "s"(seg)
+        : "memory");
+  }
+}
 
 // Operand read, contraction over the tile's columns: row `row`, logical chunk
 // `chunk` (eight consecutive columns) -> bf16x8.
