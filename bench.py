@@ -16,7 +16,8 @@ FLOP accounting (algorithmic, not what the kernels execute):
   backward  2.5 x forward;  a step is forward + backward = 3.5 x forward.
 Per kernel (for the roofline of the dominant kernel): forward kernel = 1 x
 forward (two products), dK/dV kernel = 2 x forward (four products), dQ kernel =
-1.5 x forward (three products), D pre-pass = bytes 2 * (2 * B*H*N*d) + 4 * B*H*N.
+1.5 x forward (three products; it also forms D_i = rowsum(dO * O), which is
+not counted).
 Peak: MI355X dense bf16 matrix throughput 2516.6 TFLOP/s (256 CU x 2.4 GHz x
 4096 flop/clk), HBM 8 TB/s.
 """
@@ -178,7 +179,8 @@ def main():
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
     s, causal, mb = cfg.scale, cfg.causal, cfg.mask_block
 
-    kernels = ["fwd", "dsum", "dkdv", "dq"]
+    # the launches of forward + fa_bwd (dQ with D, then dK/dV), one stage call each
+    kernels = ["fwd", "dq", "dkdv"]
 
     def step(ev=None):
         if ev is not None:
@@ -186,21 +188,19 @@ def main():
         fa.forward(q, k, v, s, causal, bmg, mb, out=o, lse=lse)
         if ev is not None:
             ev[1].record()
-        fa.bwd_dsum(o, do, dsum)
+        fa.bwd_dq_dsum(q, k, v, o, do, lse, s, causal, bmg, mb, dsum=dsum, dq=dq)
         if ev is not None:
             ev[2].record()
         fa.bwd_dkdv(q, k, v, do, lse, dsum, s, causal, bmg, mb, dk=dk, dv=dv)
         if ev is not None:
             ev[3].record()
-        fa.bwd_dq(q, k, v, do, lse, dsum, s, causal, bmg, mb, dq=dq)
-        if ev is not None:
-            ev[4].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kernels) + 1)]
+           for _ in range(args.steps)]
     start = torch.cuda.Event(enable_timing=True)
     end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -221,17 +221,12 @@ def main():
     step_flops = 3.5 * fwd_flops
     value = step_flops / (ms_per_step * 1e-3) / 1e12
     kflops = {"fwd": fwd_flops, "dkdv": 2.0 * fwd_flops, "dq": 1.5 * fwd_flops}
-    dsum_bytes = 2.0 * (2.0 * B * H * N * d) + 4.0 * B * H * N
     per_kernel = {}
     for name in kernels:
         t = kern_ms[name] * 1e-3
-        if name == "dsum":
-            per_kernel[name] = {"ms": kern_ms[name], "GB/s": dsum_bytes / t / 1e9,
-                                "frac_hbm": dsum_bytes / t / 1e9 / PEAK_HBM_GBS}
-        else:
-            tf = kflops[name] / t / 1e12
-            per_kernel[name] = {"ms": kern_ms[name], "TFLOP/s": tf,
-                                "frac_mfma": tf / PEAK_BF16_TFLOPS}
+        tf = kflops[name] / t / 1e12
+        per_kernel[name] = {"ms": kern_ms[name], "TFLOP/s": tf,
+                            "frac_mfma": tf / PEAK_BF16_TFLOPS}
     dominant = max(("fwd", "dkdv", "dq"), key=lambda n: kern_ms[n])
     achieved = per_kernel[dominant]["TFLOP/s"]
     roofline = {
@@ -244,7 +239,7 @@ def main():
         "traffic": measured_traffic(cfg.name, dominant),
     }
     fwd_tflops = fwd_flops / (kern_ms["fwd"] * 1e-3) / 1e12
-    bwd_ms = kern_ms["dsum"] + kern_ms["dkdv"] + kern_ms["dq"]
+    bwd_ms = kern_ms["dq"] + kern_ms["dkdv"]
     bwd_tflops = 2.5 * fwd_flops / (bwd_ms * 1e-3) / 1e12
     log(f"[bench] {cfg.name} B{B} H{H} N{N} d{d} causal={causal}: {ms_per_step:.3f} ms/step "
         f"(wall {wall / args.steps * 1e3:.3f}), fwd+bwd {value:.1f} TFLOP/s, fwd {fwd_tflops:.1f}, "

@@ -43,6 +43,8 @@ _SIGNATURES = {
                          _vp, _vp, _vp]),
     "fa_bwd_dq": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i,
                        _vp, _vp]),
+    "fa_bwd_dq_dsum": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i,
+                            _vp, _vp, _vp]),
     "fa_strerror": (ctypes.c_char_p, [_i]),
 }
 
@@ -258,6 +260,33 @@ def bwd_dq(q, k, v, do, lse, dsum, scale=None, causal=False, blockmask=None, mas
     if rc != FA_OK:
         raise LibfaError(rc, "fa_bwd_dq")
     return dq
+
+
+def bwd_dq_dsum(q, k, v, o, do, lse, scale=None, causal=False, blockmask=None, mask_block=128,
+                dsum=None, dq=None):
+    """dQ and D in one launch (the first half of backward); returns (dq, dsum)."""
+    torch = _torch()
+    _check(q, "q", torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(t, name, torch.bfloat16, q.shape, q.device)
+    B, H, N, d = q.shape
+    _check(lse, "lse", torch.float32, (B, H, N), q.device)
+    if dsum is None:
+        dsum = torch.empty((B, H, N), dtype=torch.float32, device=q.device)
+    _check(dsum, "dsum", torch.float32, (B, H, N), q.device)
+    scale = default_scale(d) if scale is None else float(scale)
+    dq = torch.empty_like(q) if dq is None else dq
+    _check(dq, "dq", torch.bfloat16, q.shape, q.device)
+    bm_ptr, mb = _mask_args(blockmask, N, mask_block, q.device)
+    rc = load_library().fa_bwd_dq_dsum(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                       do.data_ptr(), lse.data_ptr(), B, H, N, d, scale,
+                                       int(bool(causal)), bm_ptr, mb, dsum.data_ptr(),
+                                       dq.data_ptr(), _stream_ptr(q.device))
+    if rc != FA_OK:
+        raise LibfaError(rc, "fa_bwd_dq_dsum")
+    return dq, dsum
 
 
 class FlashAttention:

@@ -168,7 +168,23 @@ int fa_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const
     return FA_ERR_UNSUPPORTED;
   const fa::BwdParams p = bwd_params(Q, K, V, nullptr, dO, LSE, const_cast<float*>(Dsum), B, H,
                                      N, scale, blockmask, mask_block, dQ, nullptr, nullptr);
-  return status_of(fa::launch_bwd_dq(p, d, causal != 0, blockmask != nullptr, stream));
+  return status_of(fa::launch_bwd_dq(p, d, causal != 0, blockmask != nullptr, false, stream));
+}
+
+int fa_bwd_dq_dsum(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                   const float* LSE, int B, int H, int N, int d, float scale, int causal,
+                   const uint8_t* blockmask, int mask_block, float* Dsum, void* dQ,
+                   hipStream_t stream) {
+  bool empty = false;
+  int rc = check_common(B, H, N, d, scale, blockmask, mask_block, &empty);
+  if (rc != FA_OK) return rc;
+  if (empty) return FA_OK;
+  if (!Q || !K || !V || !O || !dO || !LSE || !Dsum || !dQ) return FA_ERR_NULL;
+  if (!all_aligned16({Q, K, V, O, dO, dQ}) || !aligned(LSE, 4) || !aligned(Dsum, 4))
+    return FA_ERR_UNSUPPORTED;
+  const fa::BwdParams p = bwd_params(Q, K, V, O, dO, LSE, Dsum, B, H, N, scale, blockmask,
+                                     mask_block, dQ, nullptr, nullptr);
+  return status_of(fa::launch_bwd_dq(p, d, causal != 0, blockmask != nullptr, true, stream));
 }
 
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
@@ -187,9 +203,9 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
   const fa::BwdParams p = bwd_params(Q, K, V, O, dO, LSE, static_cast<float*>(workspace), B, H,
                                      N, scale, blockmask, mask_block, dQ, dK, dV);
   const bool cz = causal != 0, sp = blockmask != nullptr;
-  rc = status_of(fa::launch_bwd_dsum(p, d, stream));
+  // dQ first, forming D on the way (the same bits fa_bwd_dsum writes), then dK, dV
+  rc = status_of(fa::launch_bwd_dq(p, d, cz, sp, true, stream));
   if (rc == FA_OK) rc = status_of(fa::launch_bwd_dkdv(p, d, cz, sp, stream));
-  if (rc == FA_OK) rc = status_of(fa::launch_bwd_dq(p, d, cz, sp, stream));
   return rc;
 }
 

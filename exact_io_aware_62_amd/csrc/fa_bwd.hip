@@ -7,7 +7,7 @@
 //   dV = P^T dO,  dP = dO V^T,  D_i = sum_j P_ij dP_ij = sum_k dO_ik O_ik,
 //   dS = P * (dP - D),  dQ = scale * dS K,  dK = scale * dS^T Q.
 //
-// Three launches, all deterministic (no atomics; FlashAttention-2 wiki,
+// Three kernels, all deterministic (no atomics; FlashAttention-2 wiki,
 // "性能与效率": exact and deterministic):
 //   1. dsum_kernel   D_i from the O actually handed in (bf16) and dO;
 //   2. dkdv_kernel   one workgroup per 128 keys of one head, looping over
@@ -15,6 +15,8 @@
 //                    written once;
 //   3. dq_kernel     one workgroup per 128 query rows, looping over key
 //                    tiles: dQ accumulates in registers and is written once.
+// The full backward runs dq_kernel first with D formed inside it (bitwise
+// the value dsum_kernel gives), then dkdv_kernel: two launches.
 // Both main kernels split the sequence over workgroups the way the forward
 // does (FlashAttention-2 wiki, "技术架构与工作原理", item 2).
 
@@ -316,18 +318,31 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
 //    K^T with the LDS transpose read.  Same transposed-score arrangement as
 //    the forward: each lane owns one query row, so LSE and D are per-lane
 //    scalars.
+//
+//    Per tile the 4 NKK + 4 NDB matrix products are issued in a fixed order
+//    (S^T of key block 0, of block 1, dP^T of block 0, of block 1, dQ of
+//    block 0, of block 1), and the vector work runs under them, each piece
+//    two products after the last product whose result it reads:
+//    P = exp2(S c - lse2) of block 0 under S^T of block 1, of block 1 under
+//    dP^T of block 0, dS = P (dP - D) of block 0 under dP^T of block 1, of
+//    block 1 under dQ of block 0.
+//
+//    FUSED_D: the workgroup also forms D_i = sum_k dO_ik O_ik for its rows
+//    and stores it, in exactly the order dsum_kernel uses (per eight-column
+//    chunk a sequential fused multiply-add, then a pairwise tree over the
+//    chunks whose index differs in bit D/16, D/32, ..., 1), so the result is
+//    the same to the bit; the dK/dV kernel then reads it.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool SPARSE>
+template <int D, bool CAUSAL, bool SPARSE, bool FUSED_D>
 __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   constexpr int BQ = 128, BK = 64, NW = 4;
   constexpr int NDB = D / 32, NKK = D / 16;
   using T = LdsTile<BK, D>;
   constexpr int RB = T::kRowBytes;
-  // K and V tiles, two stages, in separate arrays (see dkdv_kernel)
-  __shared__ __attribute__((aligned(1024))) char kbuf0[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) char kbuf1[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) char vbuf0[T::kBytes];
-  __shared__ __attribute__((aligned(1024))) char vbuf1[T::kBytes];
+  // two stages of the K and V tiles, filled by copy_async; the stage is
+  // chosen at run time so one loop body serves both
+  __shared__ __attribute__((aligned(1024))) char kbuf[2 * T::kBytes];
+  __shared__ __attribute__((aligned(1024))) char vbuf[2 * T::kBytes];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
@@ -349,7 +364,36 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     of[kk] = as_bf16x8(qrow < N ? ldg16(p.dO + head + off) : zero_u32x4());
   }
   const float lse2 = qrow < N ? lse_to_log2(p.LSE[(size_t)bc.bh * N + qrow]) : INFINITY;
-  const float dsum = qrow < N ? p.Dsum[(size_t)bc.bh * N + qrow] : 0.f;
+  float dsum;
+  if constexpr (FUSED_D) {
+    // chunk c = 2 kk + g of the row (columns 8c .. 8c+7) is in of[kk]
+    float part[NKK];
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      const u32x4 o = qrow < N ? ldg16(p.O + head + (size_t)qrow * D + kk * 16 + g * 8)
+                               : zero_u32x4();
+      const u32x4 gd = __builtin_bit_cast(u32x4, of[kk]);
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc = __builtin_fmaf(__uint_as_float(o[i] << 16), __uint_as_float(gd[i] << 16), acc);
+        acc = __builtin_fmaf(__uint_as_float(o[i] & 0xffff0000u),
+                             __uint_as_float(gd[i] & 0xffff0000u), acc);
+      }
+      part[kk] = acc;
+    }
+    // tree over chunk bits D/16 .. 2 inside the lane (kk bits NKK/2 .. 1),
+    // then chunk bit 1 (= g) across the two lane halves
+#pragma unroll
+    for (int off = NKK / 2; off > 0; off >>= 1)
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        if (!(kk & off)) part[kk] = part[kk] + part[kk | off];
+    dsum = sum_xor32(part[0]);
+    if (g == 0 && qrow < N) p.Dsum[(size_t)bc.bh * N + qrow] = dsum;
+  } else {
+    dsum = qrow < N ? p.Dsum[(size_t)bc.bh * N + qrow] : 0.f;
+  }
 
   const int kend = CAUSAL ? min(N, (qb + 1) * BQ) : N;
   const int ntiles = (kend + BK - 1) / BK;
@@ -368,76 +412,107 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   const float c = p.scale_log2;
 
   const auto lofs = T::template lane_offsets<NW>(wave, lane);
-  auto issue = [&](int t, int bufi) FA_INLINE {
-    T::template copy<NW>(Kh, t * BK, N, bufi ? kbuf1 : kbuf0, wave, lofs);
-    T::template copy<NW>(Vh, t * BK, N, bufi ? vbuf1 : vbuf0, wave, lofs);
+  auto issue = [&](int t, int stage) FA_INLINE {
+    copy_async<T, NW>(Kh, t * BK, N, lds_addr(kbuf) + stage * T::kBytes, wave, lofs);
+    copy_async<T, NW>(Vh, t * BK, N, lds_addr(vbuf) + stage * T::kBytes, wave, lofs);
   };
 
-  auto compute = [&](auto bufc, int t) FA_INLINE {
-    constexpr int BUFI = decltype(bufc)::value;
-    const char* kt = BUFI ? kbuf1 : kbuf0;
-    const char* vt = BUFI ? vbuf1 : vbuf0;
-    const int k0 = t * BK;
-    if (CAUSAL && k0 > q0w + 31) return;
-    f32x16 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = zero16();
-      dp[kb] = zero16();
+  const OperandAddr<T> oa = operand_addr<T>(lane);
+  constexpr int NS = 4 * NKK + 4 * NDB;   // products per tile
+  constexpr int PF = 3;                   // operand reads issued this many products ahead
+  // operand of product j (see the schedule above)
+  auto operand = [&](const char* kt, const char* vt, int j) FA_INLINE -> bf16x8 {
+    if (j < 4 * NKK) {
+      const char* base = j < 2 * NKK ? kt : vt;
+      const int kb = (j / NKK) & 1, kk = j % NKK;
+      return as_bf16x8(*reinterpret_cast<const u32x4*>(base + kb * 32 * RB + (oa.xr ^ (kk << 5)) +
+                                                         oa.ar));
     }
-#pragma unroll
-    for (int kk = 0; kk < NKK; ++kk)
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = mfma32x32x16(lds_row_operand<T>(kt + kb * 32 * RB, r, 2 * kk + g), qf[kk], s[kb]);
-        dp[kb] = mfma32x32x16(lds_row_operand<T>(vt + kb * 32 * RB, r, 2 * kk + g), of[kk],
-                              dp[kb]);
-      }
+    const int jj = j - 4 * NKK, kb = jj / (2 * NDB), ks2 = (jj / NDB) & 1, db = jj % NDB;
+    const char* rk = kt + (kb * 32 + 16 * ks2) * RB + (oa.xt ^ (db << 6));
+    return bf16x8_from_halves(lds_tr_b64(rk + oa.at0), lds_tr_b64(rk + oa.at1));
+  };
+
+  auto compute = [&](int stage, int t) FA_INLINE {
+    const char* kt = kbuf + stage * T::kBytes;
+    const char* vt = vbuf + stage * T::kBytes;
+    const int k0 = t * BK;
     const bool need_mask = (CAUSAL && k0 + BK - 1 > q0w) || (k0 + BK > N);
+    f32x16 s[2], dp[2];
+    bf16x8 ds[4];   // dS^T B operands, entry kb * 2 + ks2
+    s[0] = zero16(); s[1] = zero16(); dp[0] = zero16(); dp[1] = zero16();
+    bf16x8 fr[NS];
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float sv = s[kb][i];
-        if (need_mask) {
-          const int key = k0 + kb * 32 + (i >> 2) * 8 + g * 4 + (i & 3);
-          if (key >= N || (CAUSAL && key > qrow)) sv = -INFINITY;
-        }
-        const float pv = exp2_fast(__builtin_fmaf(sv, c, -lse2));
-        dp[kb][i] = pv * (dp[kb][i] - dsum);
+    for (int j = 0; j < PF; ++j) fr[j] = operand(kt, vt, j);
+    static_for<0, NS>([&](auto jc) FA_INLINE {
+      constexpr int j = decltype(jc)::value;
+      if constexpr (j < 2 * NKK) {
+        constexpr int kb = j / NKK, kk = j % NKK;
+        s[kb] = mfma32x32x16(fr[j], qf[kk], s[kb]);
+      } else if constexpr (j < 4 * NKK) {
+        constexpr int kb = (j - 2 * NKK) / NKK, kk = j % NKK;
+        dp[kb] = mfma32x32x16(fr[j], of[kk], dp[kb]);
+      } else {
+        constexpr int jj = j - 4 * NKK, kb = jj / (2 * NDB), ks2 = (jj / NDB) & 1, db = jj % NDB;
+        dq[db] = mfma32x32x16(fr[j], ds[kb * 2 + ks2], dq[db]);
       }
-    // dQ^T += K^T dS^T
+      if constexpr (j + PF < NS) fr[j + PF] = operand(kt, vt, j + PF);
+      // vector work of this product slot: unit u in 0..3 (P of block 0, P of
+      // block 1, dS of block 0, dS of block 1) runs in slots
+      // (u + 1) NKK + 2 .. (u + 2) NKK + 1, 16 / NKK elements per slot
+      static_for<0, 4>([&](auto uc) FA_INLINE {
+        constexpr int u = decltype(uc)::value;
+        constexpr int s0 = (u + 1) * NKK + 2;
+        if constexpr (j >= s0 && j < s0 + NKK) {
+          constexpr int kb = u & 1;
+          if constexpr (j == s0 && u < 2) {
+            if (need_mask) {
+              // register i holds key k0 + kb*32 + (i/4)*8 + g*4 + i%4
+              const int ln = lane_id();
+              const int kl = k0 + kb * 32 + (ln >> 5) * 4;
+              const int lim = CAUSAL ? min(N - 1, q0w + (ln & 31)) - kl : N - 1 - kl;
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) {
-        const bf16x8 sb = pack_c8(dp[kb], 8 * ks2);
-        const char* kk0 = kt + (kb * 32 + 16 * ks2) * RB;
-#pragma unroll
-        for (int db = 0; db < NDB; ++db) {
-          const bf16x8 a = bf16x8_from_halves(lds_tr_b64(kk0 + tr_offset<T>(0, db * 32, lane, 0)),
-                                              lds_tr_b64(kk0 + tr_offset<T>(0, db * 32, lane, 1)));
-          dq[db] = mfma32x32x16(a, sb, dq[db]);
+              for (int i = 0; i < 16; ++i)
+                if ((i >> 2) * 8 + (i & 3) > lim) s[kb][i] = -INFINITY;
+            }
+          }
+          constexpr int PER = 16 / NKK, i0 = (j - s0) * PER;
+          static_for<i0, i0 + PER>([&](auto ic) FA_INLINE {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (u < 2) {
+              float pv = exp2_fast(__builtin_fmaf(s[kb][i], c, -lse2));
+              pin(pv);
+              s[kb][i] = pv;
+            } else {
+              float dsv = s[kb][i] * (dp[kb][i] - dsum);
+              pin(dsv);
+              dp[kb][i] = dsv;
+              if constexpr ((i & 7) == 7) {
+                ds[kb * 2 + (i >> 3)] = pack_c8(dp[kb], i - 7);
+                pin(ds[kb * 2 + (i >> 3)]);
+              }
+            }
+          });
         }
-      }
+      });
+      __builtin_amdgcn_sched_barrier(0);
+    });
   };
 
   int t = next_tile(0);
+  int stage = 0;
   if (t < ntiles) issue(t, 0);
+  // one loop body for both stages keeps dQ in one register set
   while (t < ntiles) {
     wait_vmem();
     __syncthreads();
-    int tn = next_tile(t + 1);
-    if (tn < ntiles) issue(tn, 1);
-    compute(std::integral_constant<int, 0>{}, t);
+    const int tn = next_tile(t + 1);
+    if (tn < ntiles) issue(tn, stage ^ 1);
+    // a tile entirely above this wavefront's causal diagonal contributes 0
+    if (!(CAUSAL && t * BK > q0w + 31)) compute(stage, t);
     t = tn;
-    if (t >= ntiles) break;
-    wait_vmem();
-    __syncthreads();
-    tn = next_tile(t + 1);
-    if (tn < ntiles) issue(tn, 0);
-    compute(std::integral_constant<int, 1>{}, t);
-    t = tn;
+    stage ^= 1;
   }
 
   if (qrow < N) {
@@ -475,9 +550,12 @@ static hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
 }
 
 template <int D, bool CAUSAL, bool SPARSE>
-static hipError_t launch_dq_t(const BwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((dq_kernel<D, CAUSAL, SPARSE>), dim3((unsigned)((long long)p.nqb * p.BH)),
-                     dim3(256), 0, stream, p);
+static hipError_t launch_dq_t(const BwdParams& p, bool fused_d, hipStream_t stream) {
+  const dim3 grid((unsigned)((long long)p.nqb * p.BH));
+  if (fused_d)
+    hipLaunchKernelGGL((dq_kernel<D, CAUSAL, SPARSE, true>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((dq_kernel<D, CAUSAL, SPARSE, false>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
@@ -496,8 +574,9 @@ hipError_t launch_bwd_dkdv(const BwdParams& p, int d, bool causal, bool sparse,
   return FA_DISPATCH(launch_dkdv_t, d, causal, sparse, p, stream);
 }
 
-hipError_t launch_bwd_dq(const BwdParams& p, int d, bool causal, bool sparse, hipStream_t stream) {
-  return FA_DISPATCH(launch_dq_t, d, causal, sparse, p, stream);
+hipError_t launch_bwd_dq(const BwdParams& p, int d, bool causal, bool sparse, bool fused_d,
+                         hipStream_t stream) {
+  return FA_DISPATCH(launch_dq_t, d, causal, sparse, p, fused_d, stream);
 }
 
 }  // namespace fa

@@ -17,6 +17,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <type_traits>
 #include <stdint.h>
 
 // Lambdas that capture by reference must be inlined: an out-of-line call
@@ -102,6 +103,26 @@ __device__ __forceinline__ int lane_id() {
 }
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// f(std::integral_constant<int, I>{}) for I = B .. E-1, in order, each call
+// with a compile-time index (a loop the compiler cannot fail to unroll).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+// Keeps the computation of x at this point of the program.  An empty asm
+// statement with side effects takes x in registers and hands it back, so the
+// compiler can neither sink the work that produced x into a later basic
+// block (next to its first real use) nor move it across a neighbouring
+// scheduling barrier.  Costs no instruction.
+template <class T>
+__device__ __forceinline__ void pin(T& x) {
+  asm volatile("" : "+v"(x));
+}
 
 // max over lanes l and l ^ 32 (the two halves of a wavefront), without LDS:
 // v_permlane32_swap exchanges the upper half of one operand with the lower

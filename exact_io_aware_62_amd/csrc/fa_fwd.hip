@@ -114,14 +114,6 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     T::template copy<NW>(Vh, t * BK, N, buf ? vbuf1 : vbuf0, wave, lofs);
   };
 
-  auto rowmax = [&](const f32x16 (&s)[2]) {
-    float mx = s[0][0];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-    return mx;
-  };
   // P = exp2(S c - m), packed to the bf16 B operands of the PV product:
   // k-step ks2 of key block kb uses C registers 8*ks2 .. 8*ks2+7.
   auto exponentiate = [&](f32x16 (&s)[2], bf16x8 (&pb)[4]) {
@@ -152,10 +144,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   // product and then overwrites it with the current tile's packed P.
   bf16x8 pb[4];
 
-  // row max over this lane's scores (raw units)
-  // phase 1 for tile tc: mask, row max, move the running max if needed.
-  // Returns the factor the accumulated O must be scaled by (1 if unmoved).
-  auto phase1 = [&](int tc) FA_INLINE -> float {
+  // Scores above this wavefront's causal diagonal or past the last key -> -inf.
+  auto mask = [&](int tc) FA_INLINE {
     if (needs_mask(tc)) {
       // register i of key block kb holds key k0 + g*4 + kb*32 + (i/4)*8 + i%4;
       // compare the constant part against one per-lane bound
@@ -169,18 +159,44 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         for (int i = 0; i < 16; ++i)
           if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) sc[kb][i] = -INFINITY;
     }
-    // The running maximum only moves when a score exceeds it by more than
-    // kSlack (log2 units): every exp2 argument then stays below kSlack, far
-    // inside fp32 and bf16 range, and since the final 1/l and LSE use the
-    // same m the result is the same for any such m.  With scores of a few
-    // units this rescales O about once per row.
-    const float mxc = max_xor32(rowmax(sc)) * c;
+  };
+  // Row max of the tile as a tree of max3 (depth 4 instead of a chain of 16),
+  // in two parts so that each part fits under one matrix product.
+  float mx4[4];
+  auto rowmax_part1 = [&]() FA_INLINE {
+    float t[11];
+#pragma unroll
+    for (int u = 0; u < 10; ++u) {
+      const int e = 3 * u;
+      t[u] = __builtin_fmaxf(__builtin_fmaxf(sc[e >> 4][e & 15], sc[(e + 1) >> 4][(e + 1) & 15]),
+                             sc[(e + 2) >> 4][(e + 2) & 15]);
+    }
+    t[10] = __builtin_fmaxf(sc[1][14], sc[1][15]);
+#pragma unroll
+    for (int u = 0; u < 3; ++u) {
+      mx4[u] = __builtin_fmaxf(__builtin_fmaxf(t[3 * u], t[3 * u + 1]), t[3 * u + 2]);
+      pin(mx4[u]);
+    }
+    mx4[3] = __builtin_fmaxf(t[9], t[10]);
+    pin(mx4[3]);
+  };
+  // The running maximum only moves when a score exceeds it by more than
+  // kSlack (log2 units): every exp2 argument then stays below kSlack, far
+  // inside fp32 and bf16 range, and since the final 1/l and LSE use the
+  // same m the result is the same for any such m.  With scores of a few
+  // units this rescales O about once per row.  Returns the factor the
+  // accumulated O must be scaled by (1 if unmoved).
+  auto rowmax_part2 = [&]() FA_INLINE -> float {
+    const float mx = __builtin_fmaxf(__builtin_fmaxf(mx4[0], mx4[1]), __builtin_fmaxf(mx4[2], mx4[3]));
+    const float mxc = max_xor32(mx) * c;
     float alpha = 1.f;
     if (mxc > m_run + kSlack) {
       alpha = exp2_fast(m_run - mxc);
       m_run = mxc;
       l_run *= alpha;
     }
+    pin(m_run);
+    pin(alpha);
     return alpha;
   };
 
@@ -195,12 +211,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     const char* vk = vt + (kb * 32 + 16 * ks2) * RB + (oa.xt ^ (db << 6));
     return bf16x8_from_halves(lds_tr_b64(vk + oa.at0), lds_tr_b64(vk + oa.at1));
   };
-  // phase B: O += P_prev V_prev on the matrix cores, interleaved with
-  // P = exp2(S c - m) of the current tile, its bf16 packing and row sum.
-  // Program order is the issue order (each step is fenced): V^T fragments
-  // are read PF products ahead, the vector work is spread evenly.
-  auto phaseB = [&](const char* vt) FA_INLINE {
-    constexpr int NJ = 4 * NDB, PF = 2;
+  // phase B: O += P_prev V_prev on the matrix cores, interleaved with the
+  // current tile's softmax: its row max under the first products, then
+  // P = exp2(S c - m), its bf16 packing and row sum under the rest.
+  // Program order is the issue order (each step is fenced; pin() keeps the
+  // vector work where it is placed): V^T fragments are read PF products ahead.
+  auto phaseB = [&](const char* vt, float& alpha) FA_INLINE {
+    constexpr int NJ = 4 * NDB, PF = 2, J0 = 2;   // exps in products J0 .. NJ-1
     bf16x8 vfr[NJ];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -211,17 +228,30 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       const int kb = j / (2 * NDB), ks2 = (j / NDB) & 1, db = j % NDB;
       oacc[db] = mfma32x32x16(vfr[j], pb[kb * 2 + ks2], oacc[db]);
       if (j + PF < NJ) vfr[j + PF] = vread(vt, j + PF);
-      // P entry q = j / NDB is last read by product j = NDB q + NDB - 1 and
-      // is repacked right after it (exps 8q .. 8q+7 fall in those steps)
+      if (j == 0) rowmax_part1();
+      if (j == 1) alpha = rowmax_part2();
+      // P entry q is last read by product NDB q + NDB - 1; its exps come later
+      // (entry q's exps end by product J0 + (8q + 8) (NJ - J0) / 32 - 1 >= NDB q + NDB - 1)
+      constexpr int NE = NJ - J0;
 #pragma unroll
-      for (int e = j * 32 / NJ; e < (j + 1) * 32 / NJ; ++e) {
+      for (int e = j < J0 ? 0 : (j - J0) * 32 / NE; e < (j < J0 ? 0 : (j + 1 - J0) * 32 / NE); ++e) {
         const int b = e >> 4, i = e & 15;
         // the row sum is taken over the fp32 probabilities: a sum of the
         // bf16-rounded ones would move LSE by up to 2^-9 on short rows
-        const float pe = exp2_fast(__builtin_fmaf(sc[b][i], c, -m_run));
+        float pe = exp2_fast(__builtin_fmaf(sc[b][i], c, -m_run));
+        pin(pe);
         sc[b][i] = pe;
-        if (e & 1) a1 += pe; else a0 += pe;
-        if ((i & 7) == 7) pb[b * 2 + (i >> 3)] = pack_c8(sc[b], i - 7);
+        if (e & 1) {
+          a1 += pe;
+          pin(a1);
+        } else {
+          a0 += pe;
+          pin(a0);
+        }
+        if ((i & 7) == 7) {
+          pb[b * 2 + (i >> 3)] = pack_c8(sc[b], i - 7);
+          pin(pb[b * 2 + (i >> 3)]);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -288,12 +318,16 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     // like any other: the mask sets all its scores to -inf, so its P is 0
     // and O is unchanged.  One code path keeps O in one register set.
     phaseA(PAR ? kbuf1 : kbuf0);
-    const float alpha = phase1(tc);
+    mask(tc);
     if constexpr (FIRST) {
+      rowmax_part1();
+      rowmax_part2();
       exponentiate(sc, pb);
       l_run += rowsum(sc);
     } else {
-      l_run += phaseB(PAR ? vbuf0 : vbuf1);
+      float alpha;
+      const float psum = phaseB(PAR ? vbuf0 : vbuf1, alpha);   // scales l_run by alpha
+      l_run += psum;
       rescale(alpha);
     }
     tc = tn;

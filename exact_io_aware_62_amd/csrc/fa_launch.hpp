@@ -48,6 +48,8 @@ hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool sparse, hipSt
 hipError_t launch_bwd_dsum(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdParams& p, int d, bool causal, bool sparse,
                            hipStream_t stream);
-hipError_t launch_bwd_dq(const BwdParams& p, int d, bool causal, bool sparse, hipStream_t stream);
+// fused_d: also form D_i and store it in p.Dsum (else read it from there)
+hipError_t launch_bwd_dq(const BwdParams& p, int d, bool causal, bool sparse, bool fused_d,
+                         hipStream_t stream);
 
 }  // namespace fa

@@ -133,8 +133,8 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
  * The three stages of fa_bwd as separate calls, for callers that schedule
  * them themselves (for example fa_bwd_dkdv and fa_bwd_dq on two streams once
  * fa_bwd_dsum has finished: they read the same inputs and write disjoint
- * outputs).  fa_bwd is exactly fa_bwd_dsum, then fa_bwd_dkdv, then fa_bwd_dq
- * on one stream.  Arguments mean what they mean for fa_bwd; Dsum is the
+ * outputs).  fa_bwd_dsum, then fa_bwd_dkdv, then fa_bwd_dq on one stream
+ * give the same bits as fa_bwd.  Arguments mean what they mean for fa_bwd; Dsum is the
  * float32 [B, H, N] buffer of D_i = sum_k dO_ik * O_ik (the workspace of
  * fa_bwd), written by fa_bwd_dsum and read by the other two.  Same errors
  * as fa_bwd, with FA_ERR_NULL for a NULL Dsum.
@@ -153,6 +153,20 @@ int fa_bwd_dq(const void* Q, const void* K, const void* V, const void* dO,
               int B, int H, int N, int d, float scale, int causal,
               const uint8_t* blockmask, int mask_block,
               void* dQ, hipStream_t stream);
+
+/*
+ * fa_bwd_dq and fa_bwd_dsum in one launch: dQ as fa_bwd_dq gives it, and D
+ * written to Dsum with the same bits fa_bwd_dsum writes (the workgroup
+ * forms D for its own rows before its main loop, summing in the same
+ * order).  fa_bwd is exactly this call, then fa_bwd_dkdv, on one stream.
+ * O is read only for D.  Errors as fa_bwd_dq, with FA_ERR_NULL for a NULL
+ * O and FA_ERR_UNSUPPORTED for a misaligned one.
+ */
+int fa_bwd_dq_dsum(const void* Q, const void* K, const void* V, const void* O,
+                   const void* dO, const float* LSE,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const uint8_t* blockmask, int mask_block,
+                   float* Dsum, void* dQ, hipStream_t stream);
 
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_strerror(int status);

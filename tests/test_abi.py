@@ -24,7 +24,7 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = fa.header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_strerror",
-                          "fa_bwd_dsum", "fa_bwd_dkdv", "fa_bwd_dq"}
+                          "fa_bwd_dsum", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dq_dsum"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -59,6 +59,12 @@ def dq(lib, q=FAKE, k=FAKE, v=FAKE, do=FAKE, lse=FAKE, dsum=FAKE, B=1, H=1, N=12
     return lib.fa_bwd_dq(q, k, v, do, lse, dsum, B, H, N, d, scale, causal, bm, mb, dq, None)
 
 
+def dqd(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, B=1, H=1, N=128, d=64,
+        scale=0.125, causal=0, bm=None, mb=0, dsum=FAKE, dq=FAKE):
+    return lib.fa_bwd_dq_dsum(q, k, v, o, do, lse, B, H, N, d, scale, causal, bm, mb, dsum, dq,
+                              None)
+
+
 def dsum(lib, o=FAKE, do=FAKE, B=1, H=1, N=128, d=64, out=FAKE):
     return lib.fa_bwd_dsum(o, do, B, H, N, d, out, None)
 
@@ -69,7 +75,7 @@ def test_stage_entry_points_validate(lib):
     assert dsum(lib, out=None) == fa.FA_ERR_NULL
     assert dsum(lib, o=None, do=None, out=None, N=0) == fa.FA_OK
     assert dsum(lib, o=FAKE + 2) == fa.FA_ERR_UNSUPPORTED
-    for call in (dkdv, dq):
+    for call in (dkdv, dq, dqd):
         assert call(lib, N=-5) == fa.FA_ERR_SHAPE
         assert call(lib, scale=float("nan")) == fa.FA_ERR_UNSUPPORTED
         assert call(lib, bm=FAKE, mb=100) == fa.FA_ERR_UNSUPPORTED
@@ -78,9 +84,14 @@ def test_stage_entry_points_validate(lib):
         assert call(lib, lse=FAKE + 1) == fa.FA_ERR_UNSUPPORTED
     assert dkdv(lib, dk=None) == fa.FA_ERR_NULL
     assert dq(lib, dq=None) == fa.FA_ERR_NULL
+    assert dqd(lib, dq=None) == fa.FA_ERR_NULL
+    assert dqd(lib, o=None) == fa.FA_ERR_NULL
+    assert dqd(lib, o=FAKE + 8) == fa.FA_ERR_UNSUPPORTED
+    assert dqd(lib, N=0, q=None, k=None, v=None, o=None, do=None, lse=None, dsum=None,
+               dq=None) == fa.FA_OK
 
 
-@pytest.mark.parametrize("call", [fwd, bwd, dkdv, dq])
+@pytest.mark.parametrize("call", [fwd, bwd, dkdv, dq, dqd])
 def test_shape_and_domain_errors(lib, call):
     assert call(lib, B=-1) == fa.FA_ERR_SHAPE
     assert call(lib, H=-2) == fa.FA_ERR_SHAPE

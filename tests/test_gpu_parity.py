@@ -180,6 +180,40 @@ def test_bitwise_deterministic(fa):
     assert _same(s1, s2)
 
 
+STAGED = [
+    # B, H, N, d, mask
+    (2, 2, 448, 128, "causal"),
+    (2, 2, 200, 64, "dense"),
+    (1, 2, 512, 64, "butterfly"),
+    (1, 1, 333, 128, "random_holes_causal"),
+]
+
+
+@pytest.mark.parametrize("case", STAGED, ids=[f"B{c[0]}H{c[1]}N{c[2]}d{c[3]}-{c[4]}"
+                                              for c in STAGED])
+def test_stage_calls_match_fa_bwd_bitwise(fa, case):
+    """fa_bwd (dQ with D formed inside, then dK/dV), fa_bwd_dq_dsum and the
+    three separate stage calls all give the same bits."""
+    torch = torch_mod()
+    B, H, N, d, kind = case
+    rng = np.random.default_rng(31)
+    causal, bm = _mask_for(kind, N, 128, rng)
+    bits = synth.draw_inputs(B, H, N, d, 31)
+    s = float(np.float32(d ** -0.5))
+    q, k, v, do = (to_gpu(bits[x]) for x in ("q", "k", "v", "do"))
+    bmg = mask_to_gpu(bm)
+    o, lse = fa.forward(q, k, v, s, causal, bmg, 128)
+    dq, dk, dv = fa.backward(q, k, v, o, do, lse, s, causal, bmg, 128)
+    dsum = fa.bwd_dsum(o, do)
+    dk2, dv2 = fa.bwd_dkdv(q, k, v, do, lse, dsum, s, causal, bmg, 128)
+    dq2 = fa.bwd_dq(q, k, v, do, lse, dsum, s, causal, bmg, 128)
+    dq3, dsum3 = fa.bwd_dq_dsum(q, k, v, o, do, lse, s, causal, bmg, 128)
+    torch.cuda.synchronize()
+    assert torch.equal(dsum, dsum3)
+    assert torch.equal(dq, dq2) and torch.equal(dq, dq3)
+    assert torch.equal(dk, dk2) and torch.equal(dv, dv2)
+
+
 def test_mask_reductions_bitwise(fa):
     B, H, N, d = 1, 2, 512, 128
     bits = synth.draw_inputs(B, H, N, d, 5)
