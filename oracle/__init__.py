@@ -21,3 +21,12 @@ from .attention import (  # noqa: F401
     backward,
     forward_rows,
 )
+from .dropout import (  # noqa: F401
+    philox4x32_10,
+    drop_threshold,
+    keep_mask,
+    head_forward_dropout,
+    head_backward_dropout,
+    forward_dropout,
+    backward_dropout,
+)
