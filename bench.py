@@ -134,6 +134,9 @@ def main():
     ap.add_argument("--steps", type=int, default=30)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="C3", choices=sorted(synth.CONFIGS))
+    ap.add_argument("--dropout", type=float, default=0.0,
+                    help="dropout probability on P (0 = none, the default workload); with "
+                         "p > 0 the step is fa_fwd_dropout + fa_bwd_dropout, timed as two parts")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the oracle timed on host cores (0 disables it)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -181,8 +184,28 @@ def main():
 
     # the launches of forward + fa_bwd (dQ with D, then dK/dV), one stage call each
     kernels = ["fwd", "dq", "dkdv"]
+    pdrop = float(args.dropout)
+    dseed, doff = 20261202, 0
+    if pdrop > 0:
+        kernels = ["fwd", "bwd"]
+
+    def step_dropout(ev=None):
+        if ev is not None:
+            ev[0].record()
+        fa.forward(q, k, v, s, causal, bmg, mb, out=o, lse=lse, dropout_p=pdrop, seed=dseed,
+                   offset=doff)
+        if ev is not None:
+            ev[1].record()
+        fa.backward(q, k, v, o, do, lse, s, causal, bmg, mb, workspace=ws, dq=dq, dk=dk, dv=dv,
+                    dropout_p=pdrop, seed=dseed, offset=doff)
+        if ev is not None:
+            ev[2].record()
+
+    ws = torch.empty(fa.bwd_workspace_bytes(B, H, N, d), dtype=torch.uint8, device=dev)
 
     def step(ev=None):
+        if pdrop > 0:
+            return step_dropout(ev)
         if ev is not None:
             ev[0].record()
         fa.forward(q, k, v, s, causal, bmg, mb, out=o, lse=lse)
@@ -220,14 +243,17 @@ def main():
     fwd_flops = 4.0 * B * H * N * N * d * frac
     step_flops = 3.5 * fwd_flops
     value = step_flops / (ms_per_step * 1e-3) / 1e12
-    kflops = {"fwd": fwd_flops, "dkdv": 2.0 * fwd_flops, "dq": 1.5 * fwd_flops}
+    kflops = {"fwd": fwd_flops, "dkdv": 2.0 * fwd_flops, "dq": 1.5 * fwd_flops,
+              "bwd": 2.5 * fwd_flops}
     per_kernel = {}
     for name in kernels:
         t = kern_ms[name] * 1e-3
         tf = kflops[name] / t / 1e12
         per_kernel[name] = {"ms": kern_ms[name], "TFLOP/s": tf,
                             "frac_mfma": tf / PEAK_BF16_TFLOPS}
-    dominant = max(("fwd", "dkdv", "dq"), key=lambda n: kern_ms[n])
+    # the dominant single kernel (with dropout the backward's two launches are timed
+    # together, so the forward is the one single-kernel figure)
+    dominant = "fwd" if pdrop > 0 else max(("fwd", "dkdv", "dq"), key=lambda n: kern_ms[n])
     achieved = per_kernel[dominant]["TFLOP/s"]
     roofline = {
         "bound": "mfma",
@@ -239,7 +265,7 @@ def main():
         "traffic": measured_traffic(cfg.name, dominant),
     }
     fwd_tflops = fwd_flops / (kern_ms["fwd"] * 1e-3) / 1e12
-    bwd_ms = kern_ms["dq"] + kern_ms["dkdv"]
+    bwd_ms = kern_ms["bwd"] if pdrop > 0 else kern_ms["dq"] + kern_ms["dkdv"]
     bwd_tflops = 2.5 * fwd_flops / (bwd_ms * 1e-3) / 1e12
     log(f"[bench] {cfg.name} B{B} H{H} N{N} d{d} causal={causal}: {ms_per_step:.3f} ms/step "
         f"(wall {wall / args.steps * 1e3:.3f}), fwd+bwd {value:.1f} TFLOP/s, fwd {fwd_tflops:.1f}, "
@@ -256,7 +282,7 @@ def main():
                "lse": lambda b, h: lse[b, h].cpu().numpy().astype(np.float64)}
     cpu = None
     parity = None
-    if args.cpu_seconds > 0:
+    if args.cpu_seconds > 0 and pdrop == 0:
         cpu, parity = cpu_baseline(cfg, bits, args.cpu_seconds, gpu_out)
         log(f"[bench] oracle on host: {cpu}")
         log(f"[bench] parity on the oracle's heads: {parity}")
@@ -277,9 +303,10 @@ def main():
         "data": "synthetic",
         "config": {
             "workload": (f"{cfg.name}: attention forward+backward, B={B} H={H} N={N} d={d}, "
-                         f"{'causal' if causal else ('butterfly block-sparse' if bm is not None else 'dense')}"),
+                         f"{'causal' if causal else ('butterfly block-sparse' if bm is not None else 'dense')}"
+                         + (f", dropout p={pdrop}" if pdrop > 0 else "")),
             "global_batch": B, "heads": H, "seq_len": N, "head_dim": d, "causal": causal,
-            "parallelism": "single GPU",
+            "dropout": pdrop, "parallelism": "single GPU",
         },
         "frac_of_peak": value / PEAK_BF16_TFLOPS,
         "fwd_tflops": fwd_tflops,

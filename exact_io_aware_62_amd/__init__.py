@@ -33,6 +33,7 @@ FA_ERR_HIP = 5
 _lib = None
 
 _vp, _i, _f, _sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+_u64, _u32 = ctypes.c_uint64, ctypes.c_uint32
 _SIGNATURES = {
     "fa_fwd": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i, _vp, _vp, _vp]),
     "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i]),
@@ -45,6 +46,11 @@ _SIGNATURES = {
                        _vp, _vp]),
     "fa_bwd_dq_dsum": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i,
                             _vp, _vp, _vp]),
+    "fa_fwd_dropout": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i, _f, _u64, _u32,
+                            _vp, _vp, _vp]),
+    "fa_bwd_dropout": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i,
+                            _f, _u64, _u32, _vp, _vp, _vp, _vp, _sz, _vp]),
+    "fa_dropout_keep_mask": (_i, [_i, _i, _i, _f, _u64, _u32, _vp, _vp]),
     "fa_strerror": (ctypes.c_char_p, [_i]),
 }
 
@@ -132,8 +138,12 @@ def default_scale(d: int) -> float:
 
 
 def forward(q, k, v, scale: float | None = None, causal: bool = False, blockmask=None,
-            mask_block: int = 128, out=None, lse=None):
-    """O, LSE = attention forward.  Returns (o [B,H,N,d] bf16, lse [B,H,N] fp32)."""
+            mask_block: int = 128, out=None, lse=None, dropout_p: float = 0.0, seed: int = 0,
+            offset: int = 0):
+    """O, LSE = attention forward.  Returns (o [B,H,N,d] bf16, lse [B,H,N] fp32).
+
+    dropout_p > 0 runs fa_fwd_dropout with that (p, seed, offset); pass the same
+    three to ``backward``."""
     torch = _torch()
     _check(q, "q", torch.bfloat16)
     if q.dim() != 4:
@@ -152,6 +162,14 @@ def forward(q, k, v, scale: float | None = None, causal: bool = False, blockmask
     else:
         _check(lse, "lse", torch.float32, (B, H, N), dev)
     bm_ptr, mb = _mask_args(blockmask, N, mask_block, dev)
+    if dropout_p:
+        rc = load_library().fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, d,
+                                           scale, int(bool(causal)), bm_ptr, mb,
+                                           float(dropout_p), int(seed), int(offset),
+                                           out.data_ptr(), lse.data_ptr(), _stream_ptr(dev))
+        if rc != FA_OK:
+            raise LibfaError(rc, "fa_fwd_dropout")
+        return out, lse
     rc = load_library().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, d, scale,
                                int(bool(causal)), bm_ptr, mb, out.data_ptr(), lse.data_ptr(),
                                _stream_ptr(dev))
@@ -161,8 +179,12 @@ def forward(q, k, v, scale: float | None = None, causal: bool = False, blockmask
 
 
 def backward(q, k, v, o, do, lse, scale: float | None = None, causal: bool = False,
-             blockmask=None, mask_block: int = 128, workspace=None, dq=None, dk=None, dv=None):
-    """dQ, dK, dV of sum(dO * O).  Returns three [B,H,N,d] bf16 tensors."""
+             blockmask=None, mask_block: int = 128, workspace=None, dq=None, dk=None, dv=None,
+             dropout_p: float = 0.0, seed: int = 0, offset: int = 0):
+    """dQ, dK, dV of sum(dO * O).  Returns three [B,H,N,d] bf16 tensors.
+
+    dropout_p > 0 runs fa_bwd_dropout (the forward must have used the same
+    dropout_p, seed and offset)."""
     torch = _torch()
     _check(q, "q", torch.bfloat16)
     if q.dim() != 4:
@@ -184,14 +206,32 @@ def backward(q, k, v, o, do, lse, scale: float | None = None, causal: bool = Fal
     if workspace is None:
         workspace = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=dev)
     bm_ptr, mb = _mask_args(blockmask, N, mask_block, dev)
-    rc = load_library().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
-                               do.data_ptr(), lse.data_ptr(), B, H, N, d, scale,
-                               int(bool(causal)), bm_ptr, mb, outs[0].data_ptr(),
-                               outs[1].data_ptr(), outs[2].data_ptr(), workspace.data_ptr(),
-                               workspace.numel() * workspace.element_size(), _stream_ptr(dev))
+    ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_ptr(dev))
+    ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
+            lse.data_ptr(), B, H, N, d, scale, int(bool(causal)), bm_ptr, mb)
+    grads = (outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr())
+    if dropout_p:
+        rc = load_library().fa_bwd_dropout(*ptrs, float(dropout_p), int(seed), int(offset),
+                                           *grads, *ws)
+        if rc != FA_OK:
+            raise LibfaError(rc, "fa_bwd_dropout")
+        return tuple(outs)
+    rc = load_library().fa_bwd(*ptrs, *grads, *ws)
     if rc != FA_OK:
         raise LibfaError(rc, "fa_bwd")
     return tuple(outs)
+
+
+def dropout_keep_mask(B: int, H: int, N: int, dropout_p: float, seed: int = 0, offset: int = 0,
+                      device="cuda"):
+    """The dropout stream's keep decisions as a uint8 [B, H, N, N] tensor (1 = kept)."""
+    torch = _torch()
+    keep = torch.empty((B, H, N, N), dtype=torch.uint8, device=device)
+    rc = load_library().fa_dropout_keep_mask(B, H, N, float(dropout_p), int(seed), int(offset),
+                                             keep.data_ptr(), _stream_ptr(keep.device))
+    if rc != FA_OK:
+        raise LibfaError(rc, "fa_dropout_keep_mask")
+    return keep
 
 
 def bwd_dsum(o, do, dsum=None):

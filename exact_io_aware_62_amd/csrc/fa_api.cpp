@@ -77,6 +77,60 @@ fa::BwdParams bwd_params(const void* Q, const void* K, const void* V, const void
 
 int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
 
+// Dropout arguments: 0 <= p < 1 (finite).  p == 0 is no dropout at all.
+int check_dropout(float p_drop) {
+  if (!std::isfinite(p_drop) || p_drop < 0.f || p_drop >= 1.f) return FA_ERR_UNSUPPORTED;
+  return FA_OK;
+}
+
+// The kernels' dropout fields: drop iff the Philox word < floor(p * 2^32);
+// kept values are multiplied by 1 / (1 - p) (fp32).
+template <class Params>
+void set_dropout(Params& p, float p_drop, uint64_t seed, uint32_t offset) {
+  const double t = std::floor((double)p_drop * 4294967296.0);
+  p.drop_thresh = t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+  p.drop_scale = 1.0f / (1.0f - p_drop);
+  p.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
+  p.seed_hi = (uint32_t)(seed >> 32);
+  p.drop_offset = offset;
+}
+
+int fwd_impl(const void* Q, const void* K, const void* V, int B, int H, int N, int d,
+             float scale, int causal, const uint8_t* blockmask, int mask_block, float p_drop,
+             uint64_t seed, uint32_t offset, void* O, float* LSE, hipStream_t stream) {
+  bool empty = false;
+  int rc = check_common(B, H, N, d, scale, blockmask, mask_block, &empty);
+  if (rc != FA_OK) return rc;
+  rc = check_dropout(p_drop);
+  if (rc != FA_OK) return rc;
+  if (empty) return FA_OK;
+  if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
+  if (!all_aligned16({Q, K, V, O}) || !aligned(LSE, 4)) return FA_ERR_UNSUPPORTED;
+
+  fa::FwdParams p;
+  p.Q = static_cast<const uint16_t*>(Q);
+  p.K = static_cast<const uint16_t*>(K);
+  p.V = static_cast<const uint16_t*>(V);
+  p.O = static_cast<uint16_t*>(O);
+  p.LSE = LSE;
+  p.blockmask = blockmask;
+  p.BH = B * H;
+  p.N = N;
+  p.nqb = (N + 127) / 128;
+  p.mask_block = blockmask ? mask_block : 128;
+  p.nbm = (N + p.mask_block - 1) / p.mask_block;
+  p.scale_log2 = scale * kLog2e;
+  set_dropout(p, p_drop, seed, offset);
+  return status_of(
+      fa::launch_fwd(p, d, causal != 0, blockmask != nullptr, p_drop > 0.f, stream));
+}
+
+int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+             const float* LSE, int B, int H, int N, int d, float scale, int causal,
+             const uint8_t* blockmask, int mask_block, float p_drop, uint64_t seed,
+             uint32_t offset, void* dQ, void* dK, void* dV, void* workspace,
+             size_t workspace_bytes, hipStream_t stream);
+
 }  // namespace
 
 extern "C" {
@@ -98,27 +152,16 @@ const char* fa_strerror(int status) {
 int fa_fwd(const void* Q, const void* K, const void* V, int B, int H, int N, int d, float scale,
            int causal, const uint8_t* blockmask, int mask_block, void* O, float* LSE,
            hipStream_t stream) {
-  bool empty = false;
-  int rc = check_common(B, H, N, d, scale, blockmask, mask_block, &empty);
-  if (rc != FA_OK) return rc;
-  if (empty) return FA_OK;
-  if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
-  if (!all_aligned16({Q, K, V, O}) || !aligned(LSE, 4)) return FA_ERR_UNSUPPORTED;
+  return fwd_impl(Q, K, V, B, H, N, d, scale, causal, blockmask, mask_block, 0.f, 0, 0, O, LSE,
+                  stream);
+}
 
-  fa::FwdParams p;
-  p.Q = static_cast<const uint16_t*>(Q);
-  p.K = static_cast<const uint16_t*>(K);
-  p.V = static_cast<const uint16_t*>(V);
-  p.O = static_cast<uint16_t*>(O);
-  p.LSE = LSE;
-  p.blockmask = blockmask;
-  p.BH = B * H;
-  p.N = N;
-  p.nqb = (N + 127) / 128;
-  p.mask_block = blockmask ? mask_block : 128;
-  p.nbm = (N + p.mask_block - 1) / p.mask_block;
-  p.scale_log2 = scale * kLog2e;
-  return status_of(fa::launch_fwd(p, d, causal != 0, blockmask != nullptr, stream));
+int fa_fwd_dropout(const void* Q, const void* K, const void* V, int B, int H, int N, int d,
+                   float scale, int causal, const uint8_t* blockmask, int mask_block,
+                   float p_drop, uint64_t seed, uint32_t offset, void* O, float* LSE,
+                   hipStream_t stream) {
+  return fwd_impl(Q, K, V, B, H, N, d, scale, causal, blockmask, mask_block, p_drop, seed,
+                  offset, O, LSE, stream);
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {
@@ -153,7 +196,7 @@ int fa_bwd_dkdv(const void* Q, const void* K, const void* V, const void* dO, con
     return FA_ERR_UNSUPPORTED;
   const fa::BwdParams p = bwd_params(Q, K, V, nullptr, dO, LSE, const_cast<float*>(Dsum), B, H,
                                      N, scale, blockmask, mask_block, nullptr, dK, dV);
-  return status_of(fa::launch_bwd_dkdv(p, d, causal != 0, blockmask != nullptr, stream));
+  return status_of(fa::launch_bwd_dkdv(p, d, causal != 0, blockmask != nullptr, false, stream));
 }
 
 int fa_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const float* LSE,
@@ -168,7 +211,8 @@ int fa_bwd_dq(const void* Q, const void* K, const void* V, const void* dO, const
     return FA_ERR_UNSUPPORTED;
   const fa::BwdParams p = bwd_params(Q, K, V, nullptr, dO, LSE, const_cast<float*>(Dsum), B, H,
                                      N, scale, blockmask, mask_block, dQ, nullptr, nullptr);
-  return status_of(fa::launch_bwd_dq(p, d, causal != 0, blockmask != nullptr, false, stream));
+  return status_of(
+      fa::launch_bwd_dq(p, d, causal != 0, blockmask != nullptr, false, false, stream));
 }
 
 int fa_bwd_dq_dsum(const void* Q, const void* K, const void* V, const void* O, const void* dO,
@@ -184,15 +228,55 @@ int fa_bwd_dq_dsum(const void* Q, const void* K, const void* V, const void* O, c
     return FA_ERR_UNSUPPORTED;
   const fa::BwdParams p = bwd_params(Q, K, V, O, dO, LSE, Dsum, B, H, N, scale, blockmask,
                                      mask_block, dQ, nullptr, nullptr);
-  return status_of(fa::launch_bwd_dq(p, d, causal != 0, blockmask != nullptr, true, stream));
+  return status_of(
+      fa::launch_bwd_dq(p, d, causal != 0, blockmask != nullptr, true, false, stream));
 }
 
 int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const void* dO,
            const float* LSE, int B, int H, int N, int d, float scale, int causal,
            const uint8_t* blockmask, int mask_block, void* dQ, void* dK, void* dV,
            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(Q, K, V, O, dO, LSE, B, H, N, d, scale, causal, blockmask, mask_block, 0.f, 0,
+                  0, dQ, dK, dV, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_dropout(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                   const float* LSE, int B, int H, int N, int d, float scale, int causal,
+                   const uint8_t* blockmask, int mask_block, float p_drop, uint64_t seed,
+                   uint32_t offset, void* dQ, void* dK, void* dV, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(Q, K, V, O, dO, LSE, B, H, N, d, scale, causal, blockmask, mask_block, p_drop,
+                  seed, offset, dQ, dK, dV, workspace, workspace_bytes, stream);
+}
+
+int fa_dropout_keep_mask(int B, int H, int N, float p_drop, uint64_t seed, uint32_t offset,
+                         uint8_t* keep, hipStream_t stream) {
+  if (B < 0 || H < 0 || N < 0) return FA_ERR_SHAPE;
+  const int rc = check_dropout(p_drop);
+  if (rc != FA_OK) return rc;
+  if ((long long)B * H * N * N > (long long)1 << 40) return FA_ERR_UNSUPPORTED;
+  if ((long long)B * H * N == 0) return FA_OK;
+  if (!keep) return FA_ERR_NULL;
+  fa::FwdParams p{};
+  p.BH = B * H;
+  p.N = N;
+  set_dropout(p, p_drop, seed, offset);
+  return status_of(fa::launch_dropout_keep_mask(p, keep, stream));
+}
+
+}  // extern "C"
+
+namespace {
+
+int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+             const float* LSE, int B, int H, int N, int d, float scale, int causal,
+             const uint8_t* blockmask, int mask_block, float p_drop, uint64_t seed,
+             uint32_t offset, void* dQ, void* dK, void* dV, void* workspace,
+             size_t workspace_bytes, hipStream_t stream) {
   bool empty = false;
   int rc = check_common(B, H, N, d, scale, blockmask, mask_block, &empty);
+  if (rc != FA_OK) return rc;
+  rc = check_dropout(p_drop);
   if (rc != FA_OK) return rc;
   if (empty) return FA_OK;
   if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL;
@@ -200,13 +284,14 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
     return FA_ERR_WORKSPACE;
   if (!all_aligned16({Q, K, V, O, dO, dQ, dK, dV}) || !aligned(LSE, 4) || !aligned(workspace, 4))
     return FA_ERR_UNSUPPORTED;
-  const fa::BwdParams p = bwd_params(Q, K, V, O, dO, LSE, static_cast<float*>(workspace), B, H,
-                                     N, scale, blockmask, mask_block, dQ, dK, dV);
-  const bool cz = causal != 0, sp = blockmask != nullptr;
+  fa::BwdParams p = bwd_params(Q, K, V, O, dO, LSE, static_cast<float*>(workspace), B, H, N,
+                               scale, blockmask, mask_block, dQ, dK, dV);
+  set_dropout(p, p_drop, seed, offset);
+  const bool cz = causal != 0, sp = blockmask != nullptr, dr = p_drop > 0.f;
   // dQ first, forming D on the way (the same bits fa_bwd_dsum writes), then dK, dV
-  rc = status_of(fa::launch_bwd_dq(p, d, cz, sp, true, stream));
-  if (rc == FA_OK) rc = status_of(fa::launch_bwd_dkdv(p, d, cz, sp, stream));
+  rc = status_of(fa::launch_bwd_dq(p, d, cz, sp, true, dr, stream));
+  if (rc == FA_OK) rc = status_of(fa::launch_bwd_dkdv(p, d, cz, sp, dr, stream));
   return rc;
 }
 
-}  // extern "C"
+}  // namespace

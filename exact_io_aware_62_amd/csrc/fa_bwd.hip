@@ -72,8 +72,16 @@ __global__ __launch_bounds__(256) void dsum_kernel(BwdParams p, long long rows) 
 //    at most 256 vector registers (two wavefronts per SIMD, no accumulator
 //    registers), and the LDS footprint lets two workgroups share a CU.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool SPARSE>
-__global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
+//    DROPOUT: dV^T += dO^T (P keep / (1 - p)) and dS = P (dP keep / (1 - p) - D).
+//    A lane holds one key and 16 queries, while one Philox draw covers four
+//    consecutive keys of one query; so the four lanes of a quad (keys
+//    4c .. 4c+3) each draw for a different query and exchange the 4-bit
+//    results with DPP quad permutes: four draws per tile instead of sixteen.
+//    The dropout draws need registers beyond the 256 the d=128 kernel fills,
+//    so that instantiation runs one workgroup per CU (with accumulator
+//    registers) rather than spill.
+template <int D, bool CAUSAL, bool SPARSE, bool DROPOUT>
+__global__ __launch_bounds__(256, (DROPOUT && D == 128) ? 1 : 2) void dkdv_kernel(BwdParams p) {
   constexpr int BKB = 128, BQ = 32, NW = 4;
   constexpr int NDB = D / 32, NKK = D / 16;
   using TQ = LdsTile<BQ, D>;    // a query tile of Q or dO
@@ -133,6 +141,14 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
     dk[db] = zero16();
   }
   const float c = p.scale_log2;
+  DropoutStream drs;
+  if constexpr (DROPOUT) {
+    drs.seed_lo = p.seed_lo;
+    drs.seed_hi = p.seed_hi;
+    drs.bh = (uint32_t)bc.bh;
+    drs.offset = p.drop_offset;
+    drs.thresh = p.drop_thresh;
+  }
 
   // Thread tid < 2*BQ carries one LSE / D value of the next tile: it is
   // loaded before that tile's LDS-DMA copies are issued (vector-memory waits
@@ -180,7 +196,26 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
   //   2. dP = dO V^T             || P = exp2(S c - lse2), packed to bf16
   //   3. dV^T += dO^T P          || dS = P (dP - D), packed to bf16
   //   4. dK^T += Q^T dS
-  auto compute = [&](int stage, int t) FA_INLINE {
+  // Dropout keep bits: bit i for register i (query q0 + (i/4)*8 + g*4 + i%4,
+  // key `key`) of the current tile; the next tile's are drawn during the
+  // current tile's last step, where the fewest registers are live.
+  uint32_t keep_cur = 0xFFFFFFFFu, keep_next = 0xFFFFFFFFu;
+  // draw m for the tile at query q0: this lane draws for query
+  // q0 + 8m + 4g + (r % 4) and keys kw + 4 (r / 4) .. +3; lane r of the quad
+  // then collects bit r % 4 of each quad lane's result
+  auto draw_keep = [&](int q0, int m) FA_INLINE {
+    const uint32_t mine =
+        drs.keep4((uint32_t)((kw >> 2) + (r >> 2)), (uint32_t)(q0 + 8 * m + 4 * g + (r & 3)));
+    const int sh = r & 3;
+    const uint32_t bits = ((quad_bcast<0>(mine) >> sh) & 1u) |
+                          (((quad_bcast<1>(mine) >> sh) & 1u) << 1) |
+                          (((quad_bcast<2>(mine) >> sh) & 1u) << 2) |
+                          (((quad_bcast<3>(mine) >> sh) & 1u) << 3);
+    keep_next = (keep_next & ~(0xFu << (4 * m))) | (bits << (4 * m));
+    pin(keep_next);
+  };
+
+  auto compute = [&](int stage, int t, int tn) FA_INLINE {
     constexpr int NJ = NKK;   // products per step (= 2 NDB)
     const char* qt = qbuf + stage * TQ::kBytes;
     const char* ot = obuf + stage * TQ::kBytes;
@@ -189,6 +224,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
     const int q0 = t * BQ;
     f32x16 s, dp;
     bf16x8 pb[2], sb[2];
+    const uint32_t keepbits = keep_cur;
     bf16x8 fa[NJ], fb[NJ];
     constexpr int PF = 2;
 
@@ -238,7 +274,18 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
         // LSE (log2 units) of the four queries of registers (i/4)*4 .. +3
         const float* lq = lse2 + (i >> 2) * 8 + g * 4;
         s[i] = exp2_fast(__builtin_fmaf(s[i], c, -lq[i & 3]));
-        if ((i & 7) == 7) pb[i >> 3] = pack_c8(s, i - 7);
+        if ((i & 7) == 7) {
+          if constexpr (DROPOUT) {
+            // dV takes the kept, rescaled probabilities; dS below takes P
+            float t8[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+              t8[e] = ((keepbits >> (i - 7 + e)) & 1u) ? s[i - 7 + e] * p.drop_scale : 0.f;
+            pb[i >> 3] = pack_bf16x8(t8[0], t8[1], t8[2], t8[3], t8[4], t8[5], t8[6], t8[7]);
+          } else {
+            pb[i >> 3] = pack_c8(s, i - 7);
+          }
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -253,7 +300,9 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
 #pragma unroll
       for (int i = j * 16 / NJ; i < (j + 1) * 16 / NJ; ++i) {
         const float* dq4 = dsum + (i >> 2) * 8 + g * 4;
-        dp[i] = s[i] * (dp[i] - dq4[i & 3]);
+        float dpv = dp[i];
+        if constexpr (DROPOUT) dpv = ((keepbits >> i) & 1u) ? dpv * p.drop_scale : 0.f;
+        dp[i] = s[i] * (dpv - dq4[i & 3]);
         if ((i & 7) == 7) sb[i >> 3] = pack_c8(dp, i - 7);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -266,6 +315,10 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
     for (int j = 0; j < NJ; ++j) {
       dk[j % NDB] = mfma32x32x16(fa[j], sb[j / NDB], dk[j % NDB]);
       if (j + PF < NJ) fa[j + PF] = tr_read(qt, j + PF);
+      if constexpr (DROPOUT) {
+        // the next tile's four draws (unused after the last tile)
+        if (j % (NJ / 4) == 0) draw_keep(tn * BQ, j / (NJ / 4));
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -275,6 +328,10 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
   if (t < nqt) {
     issue(t, 0);
     finish_issue(0);
+    if constexpr (DROPOUT) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) draw_keep(t * BQ, m);
+    }
   }
   // one loop body for both stages keeps the dK / dV accumulators in one
   // register set
@@ -283,7 +340,8 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
     __syncthreads();
     const int tn = next_tile(t + 1);
     if (tn < nqt) issue(tn, stage ^ 1);
-    compute(stage, t);
+    if constexpr (DROPOUT) keep_cur = keep_next;
+    compute(stage, t, tn);
     if (tn < nqt) finish_issue(stage ^ 1);
     t = tn;
     stage ^= 1;
@@ -333,7 +391,9 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
 //    chunks whose index differs in bit D/16, D/32, ..., 1), so the result is
 //    the same to the bit; the dK/dV kernel then reads it.
 // ---------------------------------------------------------------------------
-template <int D, bool CAUSAL, bool SPARSE, bool FUSED_D>
+//    DROPOUT: dS = P (dP keep / (1 - p) - D), with the keep bits of the tile
+//    drawn (as in the forward) while its scores are on the matrix cores.
+template <int D, bool CAUSAL, bool SPARSE, bool FUSED_D, bool DROPOUT>
 __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   constexpr int BQ = 128, BK = 64, NW = 4;
   constexpr int NDB = D / 32, NKK = D / 16;
@@ -410,6 +470,14 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
 #pragma unroll
   for (int db = 0; db < NDB; ++db) dq[db] = zero16();
   const float c = p.scale_log2;
+  DropoutStream drs;
+  if constexpr (DROPOUT) {
+    drs.seed_lo = p.seed_lo;
+    drs.seed_hi = p.seed_hi;
+    drs.bh = (uint32_t)bc.bh;
+    drs.offset = p.drop_offset;
+    drs.thresh = p.drop_thresh;
+  }
 
   const auto lofs = T::template lane_offsets<NW>(wave, lane);
   auto issue = [&](int t, int stage) FA_INLINE {
@@ -441,6 +509,9 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     f32x16 s[2], dp[2];
     bf16x8 ds[4];   // dS^T B operands, entry kb * 2 + ks2
     s[0] = zero16(); s[1] = zero16(); dp[0] = zero16(); dp[1] = zero16();
+    // keep bits: bit kb*16 + i for register i of key block kb (keys
+    // k0 + kb*32 + (i/4)*8 + g*4 + i%4 of this lane's row)
+    uint32_t keepbits = 0xFFFFFFFFu;
     bf16x8 fr[NS];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -458,6 +529,14 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
         dq[db] = mfma32x32x16(fr[j], ds[kb * 2 + ks2], dq[db]);
       }
       if constexpr (j + PF < NS) fr[j + PF] = operand(kt, vt, j + PF);
+      if constexpr (DROPOUT && j < 2 * NKK && j % (2 * NKK / 8) == 0) {
+        // eight draws per tile, spread over the S^T products
+        constexpr int u = j / (2 * NKK / 8), kb = u >> 2, m = u & 3;
+        const uint32_t bits = drs.keep4((uint32_t)(t * (BK / 4) + kb * 8 + m * 2 + g),
+                                        (uint32_t)qrow);
+        keepbits = (keepbits & ~(0xFu << (4 * u))) | (bits << (4 * u));
+        pin(keepbits);
+      }
       // vector work of this product slot: unit u in 0..3 (P of block 0, P of
       // block 1, dS of block 0, dS of block 1) runs in slots
       // (u + 1) NKK + 2 .. (u + 2) NKK + 1, 16 / NKK elements per slot
@@ -485,7 +564,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
               pin(pv);
               s[kb][i] = pv;
             } else {
-              float dsv = s[kb][i] * (dp[kb][i] - dsum);
+              float dpv = dp[kb][i];
+              if constexpr (DROPOUT)
+                dpv = ((keepbits >> (kb * 16 + i)) & 1u) ? dpv * p.drop_scale : 0.f;
+              float dsv = s[kb][i] * (dpv - dsum);
               pin(dsv);
               dp[kb][i] = dsv;
               if constexpr ((i & 7) == 7) {
@@ -543,19 +625,28 @@ hipError_t launch_bwd_dsum(const BwdParams& p, int d, hipStream_t stream) {
 }
 
 template <int D, bool CAUSAL, bool SPARSE>
-static hipError_t launch_dkdv_t(const BwdParams& p, hipStream_t stream) {
-  hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, SPARSE>), dim3((unsigned)((long long)p.nkb * p.BH)),
-                     dim3(256), 0, stream, p);
+static hipError_t launch_dkdv_t(const BwdParams& p, bool dropout, hipStream_t stream) {
+  const dim3 grid((unsigned)((long long)p.nkb * p.BH));
+  if (dropout)
+    hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, SPARSE, true>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((dkdv_kernel<D, CAUSAL, SPARSE, false>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
 template <int D, bool CAUSAL, bool SPARSE>
-static hipError_t launch_dq_t(const BwdParams& p, bool fused_d, hipStream_t stream) {
+static hipError_t launch_dq_t(const BwdParams& p, bool fused_d, bool dropout,
+                              hipStream_t stream) {
   const dim3 grid((unsigned)((long long)p.nqb * p.BH));
-  if (fused_d)
-    hipLaunchKernelGGL((dq_kernel<D, CAUSAL, SPARSE, true>), grid, dim3(256), 0, stream, p);
+  if (dropout)   // only the fused form (fa_bwd's) has a dropout instantiation
+    hipLaunchKernelGGL((dq_kernel<D, CAUSAL, SPARSE, true, true>), grid, dim3(256), 0, stream,
+                       p);
+  else if (fused_d)
+    hipLaunchKernelGGL((dq_kernel<D, CAUSAL, SPARSE, true, false>), grid, dim3(256), 0, stream,
+                       p);
   else
-    hipLaunchKernelGGL((dq_kernel<D, CAUSAL, SPARSE, false>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((dq_kernel<D, CAUSAL, SPARSE, false, false>), grid, dim3(256), 0, stream,
+                       p);
   return hipGetLastError();
 }
 
@@ -569,14 +660,15 @@ static hipError_t launch_dq_t(const BwdParams& p, bool fused_d, hipStream_t stre
                          : ((sparse) ? FN<128, false, true>(__VA_ARGS__)                  \
                                      : FN<128, false, false>(__VA_ARGS__))))
 
-hipError_t launch_bwd_dkdv(const BwdParams& p, int d, bool causal, bool sparse,
+hipError_t launch_bwd_dkdv(const BwdParams& p, int d, bool causal, bool sparse, bool dropout,
                            hipStream_t stream) {
-  return FA_DISPATCH(launch_dkdv_t, d, causal, sparse, p, stream);
+  return FA_DISPATCH(launch_dkdv_t, d, causal, sparse, p, dropout, stream);
 }
 
 hipError_t launch_bwd_dq(const BwdParams& p, int d, bool causal, bool sparse, bool fused_d,
-                         hipStream_t stream) {
-  return FA_DISPATCH(launch_dq_t, d, causal, sparse, p, fused_d, stream);
+                         bool dropout, hipStream_t stream) {
+  if (dropout && !fused_d) return hipErrorInvalidValue;
+  return FA_DISPATCH(launch_dq_t, d, causal, sparse, p, fused_d, dropout, stream);
 }
 
 }  // namespace fa

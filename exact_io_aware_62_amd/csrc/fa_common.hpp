@@ -104,6 +104,56 @@ __device__ __forceinline__ int lane_id() {
 
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers: as
+// easy as 1, 2, 3", SC 2011): ten rounds; each multiplies counter words 0 and 2
+// by two odd constants and mixes the high and low halves of the products with
+// words 1 and 3 and the round key, which advances by two Weyl constants per
+// round.  The key words are wavefront-uniform in every use here, so the key
+// schedule runs on the scalar unit.
+__device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2,
+                                               uint32_t c3, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int r = 0; r < 10; ++r) {
+    if (r) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c0;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c2;
+    const uint32_t n0 = (uint32_t)(p1 >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(p0 >> 32) ^ c3 ^ k1;
+    c1 = (uint32_t)p1;
+    c3 = (uint32_t)p0;
+    c0 = n0;
+    c2 = n2;
+  }
+  u32x4 out;
+  out[0] = c0;
+  out[1] = c1;
+  out[2] = c2;
+  out[3] = c3;
+  return out;
+}
+
+// Dropout stream of one head: element (i, j) is kept iff word j % 4 of
+// philox4x32_10(j / 4, i, bh, offset; seed) is >= thresh.  keep4 returns the
+// keep bits of keys 4*jg .. 4*jg+3 of query i in bits 0..3.
+struct DropoutStream {
+  uint32_t seed_lo, seed_hi, bh, offset, thresh;
+  __device__ __forceinline__ uint32_t keep4(uint32_t jg, uint32_t i) const {
+    const u32x4 w = philox4x32_10(jg, i, bh, offset, seed_lo, seed_hi);
+    return (uint32_t)(w[0] >= thresh) | ((uint32_t)(w[1] >= thresh) << 1) |
+           ((uint32_t)(w[2] >= thresh) << 2) | ((uint32_t)(w[3] >= thresh) << 3);
+  }
+};
+
+// Value of lane t (0..3) of this lane's group of four (DPP quad permute).
+template <int T>
+__device__ __forceinline__ uint32_t quad_bcast(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, T | (T << 2) | (T << 4) | (T << 6), 0xF,
+                                            0xF, false);
+}
+
 // f(std::integral_constant<int, I>{}) for I = B .. E-1, in order, each call
 // with a compile-time index (a loop the compiler cannot fail to unroll).
 template <int B, int E, class F>

@@ -43,7 +43,11 @@
 
 namespace fa {
 
-template <int D, bool CAUSAL, bool SPARSE>
+// DROPOUT: P is multiplied by keep / (1 - p) before the P V product (the row
+// sum, and with it LSE, stays that of the plain softmax).  The keep bits of a
+// tile come from the head's Philox stream (DropoutStream) and are drawn while
+// the tile's scores are on the matrix cores.
+template <int D, bool CAUSAL, bool SPARSE, bool DROPOUT>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   constexpr int BQ = 128, BK = 64, NW = 4;
   constexpr float kSlack = 8.0f;
@@ -105,6 +109,28 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   float m_run = kNegBig;   // running max of scaled scores (log2 domain)
   float l_run = 0.f;       // running partial row sum (this lane's keys)
   const float c = p.scale_log2;
+  // keep bits of the current tile: bit kb*16 + i for register i of key block kb
+  uint32_t keepbits = 0xFFFFFFFFu;
+  DropoutStream ds_;
+  if constexpr (DROPOUT) {
+    ds_.seed_lo = p.seed_lo;
+    ds_.seed_hi = p.seed_hi;
+    ds_.bh = (uint32_t)bc.bh;
+    ds_.offset = p.drop_offset;
+    ds_.thresh = p.drop_thresh;
+  }
+  // keys k0 + kb*32 + m*8 + g*4 + 0..3 of this lane's row, for call u = kb*4 + m
+  auto draw_keep = [&](int tc, int u) FA_INLINE {
+    const int kb = u >> 2, m = u & 3;
+    const uint32_t bits = ds_.keep4((uint32_t)(tc * (BK / 4) + kb * 8 + m * 2 + g), (uint32_t)qrow);
+    keepbits = (keepbits & ~(0xFu << (4 * u))) | (bits << (4 * u));
+    pin(keepbits);
+  };
+  // P as it enters the P V product: kept and rescaled, or 0
+  auto dropped = [&](float pe, int e) FA_INLINE -> float {
+    if constexpr (DROPOUT) return ((keepbits >> e) & 1u) ? pe * p.drop_scale : 0.f;
+    return pe;
+  };
 
   const auto lofs = T::template lane_offsets<NW>(wave, lane);
   auto load_k = [&](int t, int buf) FA_INLINE {
@@ -122,9 +148,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = exp2_fast(__builtin_fmaf(s[kb][i], c, -m_run));
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int kb = 0; kb < 2; ++kb) {
+      f32x16 t = s[kb];
 #pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) pb[kb * 2 + ks2] = pack_c8(s[kb], 8 * ks2);
+      for (int i = 0; i < 16; ++i) t[i] = dropped(s[kb][i], kb * 16 + i);
+#pragma unroll
+      for (int ks2 = 0; ks2 < 2; ++ks2) pb[kb * 2 + ks2] = pack_c8(t, 8 * ks2);
+    }
   };
   auto rowsum = [&](const f32x16 (&s)[2]) {
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
@@ -240,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         // bf16-rounded ones would move LSE by up to 2^-9 on short rows
         float pe = exp2_fast(__builtin_fmaf(sc[b][i], c, -m_run));
         pin(pe);
-        sc[b][i] = pe;
+        sc[b][i] = dropped(pe, e);
         if (e & 1) {
           a1 += pe;
           pin(a1);
@@ -273,7 +303,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     }
   };
   // scores of the tile in K buffer kt (phase A); K fragments read PF ahead
-  auto phaseA = [&](const char* kt) FA_INLINE {
+  auto phaseA = [&](const char* kt, int tc) FA_INLINE {
     // product j: k-step kk = j / 2 of key block kb = j % 2 (two independent
     // accumulation chains); one address per k-step serves both blocks
     constexpr int NJ = 2 * NKK, PF = 4;
@@ -291,6 +321,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     for (int j = 0; j < NJ; ++j) {
       sc[j & 1] = mfma32x32x16(kfr[j], qf[j >> 1], sc[j & 1]);
       if (j + PF < NJ) kread(j + PF);
+      if constexpr (DROPOUT) {
+        // eight draws per tile, spread over the score products
+        if (j % (NJ / 8) == 0) draw_keep(tc, j / (NJ / 8));
+      }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -317,7 +351,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     // A tile entirely above this wavefront's causal diagonal is processed
     // like any other: the mask sets all its scores to -inf, so its P is 0
     // and O is unchanged.  One code path keeps O in one register set.
-    phaseA(PAR ? kbuf1 : kbuf0);
+    phaseA(PAR ? kbuf1 : kbuf0, tc);
     mask(tc);
     if constexpr (FIRST) {
       rowmax_part1();
@@ -376,24 +410,58 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 }
 
 template <int D, bool CAUSAL, bool SPARSE>
-static hipError_t launch_fwd_t(const FwdParams& p, hipStream_t stream) {
-  const long long blocks = (long long)p.nqb * p.BH;
-  hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, SPARSE>), dim3((unsigned)blocks), dim3(256), 0,
-                     stream, p);
+static hipError_t launch_fwd_t(const FwdParams& p, bool dropout, hipStream_t stream) {
+  const dim3 grid((unsigned)((long long)p.nqb * p.BH));
+  if (dropout)
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, SPARSE, true>), grid, dim3(256), 0, stream, p);
+  else
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, SPARSE, false>), grid, dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool sparse, hipStream_t stream) {
+hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool sparse, bool dropout,
+                      hipStream_t stream) {
   if (d == 64) {
-    if (causal) return sparse ? launch_fwd_t<64, true, true>(p, stream)
-                              : launch_fwd_t<64, true, false>(p, stream);
-    return sparse ? launch_fwd_t<64, false, true>(p, stream)
-                  : launch_fwd_t<64, false, false>(p, stream);
+    if (causal) return sparse ? launch_fwd_t<64, true, true>(p, dropout, stream)
+                              : launch_fwd_t<64, true, false>(p, dropout, stream);
+    return sparse ? launch_fwd_t<64, false, true>(p, dropout, stream)
+                  : launch_fwd_t<64, false, false>(p, dropout, stream);
   }
-  if (causal) return sparse ? launch_fwd_t<128, true, true>(p, stream)
-                            : launch_fwd_t<128, true, false>(p, stream);
-  return sparse ? launch_fwd_t<128, false, true>(p, stream)
-                : launch_fwd_t<128, false, false>(p, stream);
+  if (causal) return sparse ? launch_fwd_t<128, true, true>(p, dropout, stream)
+                            : launch_fwd_t<128, true, false>(p, dropout, stream);
+  return sparse ? launch_fwd_t<128, false, true>(p, dropout, stream)
+                : launch_fwd_t<128, false, false>(p, dropout, stream);
+}
+
+// Keep mask of the dropout stream, keep[bh][i][j] = 1 or 0, for inspection and
+// tests: one thread per four keys of one query (one Philox draw).
+__global__ __launch_bounds__(256) void dropout_keep_mask_kernel(FwdParams p, uint8_t* keep,
+                                                               long long groups) {
+  const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= groups) return;
+  const int ng = (p.N + 3) / 4;
+  const long long row = gid / ng;            // bh * N + i
+  const int jg = (int)(gid - row * ng);
+  const int bh = (int)(row / p.N), i = (int)(row - (long long)bh * p.N);
+  DropoutStream ds;
+  ds.seed_lo = p.seed_lo;
+  ds.seed_hi = p.seed_hi;
+  ds.bh = (uint32_t)bh;
+  ds.offset = p.drop_offset;
+  ds.thresh = p.drop_thresh;
+  const uint32_t bits = ds.keep4((uint32_t)jg, (uint32_t)i);
+  uint8_t* out = keep + row * p.N + 4 * jg;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+    if (4 * jg + t < p.N) out[t] = (uint8_t)((bits >> t) & 1u);
+}
+
+hipError_t launch_dropout_keep_mask(const FwdParams& p, uint8_t* keep, hipStream_t stream) {
+  const long long groups = (long long)p.BH * p.N * ((p.N + 3) / 4);
+  const long long blocks = (groups + 255) / 256;
+  hipLaunchKernelGGL(dropout_keep_mask_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p,
+                     keep, groups);
+  return hipGetLastError();
 }
 
 }  // namespace fa

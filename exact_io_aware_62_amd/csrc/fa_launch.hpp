@@ -20,6 +20,11 @@ struct FwdParams {
   int mask_block;            // block-mask granularity (multiple of 128)
   int nbm;                   // ceil(N / mask_block)
   float scale_log2;          // scale * log2(e)
+  // dropout on P (read only by the dropout kernels): element (i, j) of head bh
+  // is kept iff philox4x32_10(j/4, i, bh, drop_offset; seed)[j % 4] >= drop_thresh
+  uint32_t drop_thresh;      // floor(p * 2^32)
+  float drop_scale;          // 1 / (1 - p), applied to kept probabilities
+  uint32_t seed_lo, seed_hi, drop_offset;
 };
 
 struct BwdParams {
@@ -42,14 +47,24 @@ struct BwdParams {
   int nbm;
   float scale;               // softmax scale
   float scale_log2;          // scale * log2(e)
+  // dropout on P (read only by the dropout kernels): element (i, j) of head bh
+  // is kept iff philox4x32_10(j/4, i, bh, drop_offset; seed)[j % 4] >= drop_thresh
+  uint32_t drop_thresh;      // floor(p * 2^32)
+  float drop_scale;          // 1 / (1 - p), applied to kept probabilities
+  uint32_t seed_lo, seed_hi, drop_offset;
 };
 
-hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool sparse, hipStream_t stream);
+// dropout: the DROPOUT instantiation (p.drop_* and p.seed_* must be set)
+hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool sparse, bool dropout,
+                      hipStream_t stream);
+// keep[bh][i][j] (uint8) of the dropout stream set in p (BH, N, drop_*, seed_*)
+hipError_t launch_dropout_keep_mask(const FwdParams& p, uint8_t* keep, hipStream_t stream);
 hipError_t launch_bwd_dsum(const BwdParams& p, int d, hipStream_t stream);
-hipError_t launch_bwd_dkdv(const BwdParams& p, int d, bool causal, bool sparse,
+hipError_t launch_bwd_dkdv(const BwdParams& p, int d, bool causal, bool sparse, bool dropout,
                            hipStream_t stream);
-// fused_d: also form D_i and store it in p.Dsum (else read it from there)
+// fused_d: also form D_i and store it in p.Dsum (else read it from there);
+// dropout: the DROPOUT instantiation, which exists only with fused_d
 hipError_t launch_bwd_dq(const BwdParams& p, int d, bool causal, bool sparse, bool fused_d,
-                         hipStream_t stream);
+                         bool dropout, hipStream_t stream);
 
 }  // namespace fa

@@ -168,6 +168,53 @@ int fa_bwd_dq_dsum(const void* Q, const void* K, const void* V, const void* O,
                    const uint8_t* blockmask, int mask_block,
                    float* Dsum, void* dQ, hipStream_t stream);
 
+/*
+ * Dropout on the attention probabilities.  The pages list dropout among the
+ * steps fused into the single attention kernel, between the softmax and the
+ * second product (FlashAttention-NeurIPS22 digest, "核心方法", Kernel
+ * fusion), and have the backward rebuild what it needs on chip ("核心方法",
+ * Backward recomputation); the mask is therefore drawn from a counter-based
+ * generator and regenerated by the backward, never stored.
+ *
+ *   P = softmax(scale * Q K^T + mask) as in fa_fwd; LSE is P's (no dropout);
+ *   O = (P * keep / (1 - p_drop)) V.
+ *
+ * Element (b, h, i, j) is kept iff word (j mod 4) of Philox4x32-10 (Salmon et
+ * al., "Parallel random numbers: as easy as 1, 2, 3", SC 2011) on the counter
+ * (j / 4, i, b * H + h, offset) under the key (seed mod 2^32, seed / 2^32) is
+ * >= floor(p_drop * 2^32).  The same (p_drop, seed, offset) must be passed to
+ * fa_bwd_dropout; a caller takes a fresh offset (or seed) per call to get a
+ * fresh mask.  p_drop must satisfy 0 <= p_drop < 1 (else FA_ERR_UNSUPPORTED);
+ * p_drop = 0 gives exactly fa_fwd / fa_bwd.  Other arguments and errors are
+ * those of fa_fwd / fa_bwd.  fa_bwd_dropout returns the gradients of
+ * sum(dO * O) for that O: dV = Pd^T dO with Pd = P * keep / (1 - p_drop), and
+ * dS = P * (dP * keep / (1 - p_drop) - D), D_i = sum_k dO_ik O_ik.
+ */
+int fa_fwd_dropout(const void* Q, const void* K, const void* V,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const uint8_t* blockmask, int mask_block,
+                   float p_drop, uint64_t seed, uint32_t offset,
+                   void* O, float* LSE, hipStream_t stream);
+
+int fa_bwd_dropout(const void* Q, const void* K, const void* V, const void* O,
+                   const void* dO, const float* LSE,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const uint8_t* blockmask, int mask_block,
+                   float p_drop, uint64_t seed, uint32_t offset,
+                   void* dQ, void* dK, void* dV,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * The keep decisions of that dropout stream as bytes: keep[((b * H + h) * N
+ * + i) * N + j] = 1 if element (b, h, i, j) is kept, else 0 (DEVICE pointer,
+ * B * H * N * N bytes, caller-owned; for inspection and tests).  Ignores
+ * masking (a masked element's probability is 0 whatever its keep bit).
+ * FA_ERR_SHAPE for negative sizes, FA_ERR_UNSUPPORTED for a bad p_drop or
+ * more than 2^40 bytes, FA_ERR_NULL for a NULL keep with a non-empty shape.
+ */
+int fa_dropout_keep_mask(int B, int H, int N, float p_drop, uint64_t seed,
+                         uint32_t offset, uint8_t* keep, hipStream_t stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_strerror(int status);
 

@@ -24,7 +24,8 @@ def lib():
 def test_exports_every_declared_symbol(lib):
     names = fa.header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_strerror",
-                          "fa_bwd_dsum", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dq_dsum"}
+                          "fa_bwd_dsum", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dq_dsum",
+                          "fa_fwd_dropout", "fa_bwd_dropout", "fa_dropout_keep_mask"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -153,3 +154,31 @@ def test_python_binding_rejects_bad_tensors():
         fa.forward(q, q, q)
     with pytest.raises(TypeError):
         fa.forward(q.float(), q, q)
+
+
+def fwdd(lib, p=0.1, B=1, H=1, N=128, d=64, scale=0.125, o=FAKE, lse=FAKE):
+    return lib.fa_fwd_dropout(FAKE, FAKE, FAKE, B, H, N, d, scale, 0, None, 0, p, 1, 2, o, lse,
+                              None)
+
+
+def bwdd(lib, p=0.1, N=128, ws=FAKE, wsb=1 << 20):
+    return lib.fa_bwd_dropout(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, N, 64, 0.125, 0, None, 0,
+                              p, 1, 2, FAKE, FAKE, FAKE, ws, wsb, None)
+
+
+def test_dropout_entry_points_validate(lib):
+    for bad in (-0.1, 1.0, 1.5, float("nan"), float("inf")):
+        assert fwdd(lib, p=bad) == fa.FA_ERR_UNSUPPORTED
+        assert bwdd(lib, p=bad) == fa.FA_ERR_UNSUPPORTED
+        assert lib.fa_dropout_keep_mask(1, 1, 8, bad, 0, 0, FAKE, None) == fa.FA_ERR_UNSUPPORTED
+    assert fwdd(lib, d=96) == fa.FA_ERR_UNSUPPORTED
+    assert fwdd(lib, B=-1) == fa.FA_ERR_SHAPE
+    assert fwdd(lib, o=None) == fa.FA_ERR_NULL
+    assert fwdd(lib, N=0, o=None, lse=None) == fa.FA_OK
+    assert bwdd(lib, ws=None) == fa.FA_ERR_WORKSPACE
+    assert bwdd(lib, N=0, ws=None) == fa.FA_OK
+    assert lib.fa_dropout_keep_mask(-1, 1, 8, 0.5, 0, 0, FAKE, None) == fa.FA_ERR_SHAPE
+    assert lib.fa_dropout_keep_mask(1, 1, 8, 0.5, 0, 0, None, None) == fa.FA_ERR_NULL
+    assert lib.fa_dropout_keep_mask(1, 1, 0, 0.5, 0, 0, None, None) == fa.FA_OK
+    assert lib.fa_dropout_keep_mask(64, 64, 1 << 17, 0.5, 0, 0, FAKE, None) == \
+        fa.FA_ERR_UNSUPPORTED
