@@ -36,12 +36,16 @@ def allowed_mask(n_q: int, n_k: int, causal: bool = False, blockmask=None,
                  mask_block: int = 128) -> np.ndarray:
     """Boolean [n_q, n_k]: True where query i may attend to key j.
 
-    Causal: key j is masked when j > i.  Block-sparse: masked when the covering
-    block of ``blockmask`` is zero.  Both may apply; a key is visible iff both allow.
+    Causal: key j is masked when j > i + (n_k - n_q), i.e. the n_q queries are the
+    last n_q positions of the n_k-long key sequence (the decoding case with a KV
+    cache, which the pages leave untreated; with n_q == n_k this is j > i).  Rows
+    with i + n_k - n_q < 0 see no key.  Block-sparse: masked when the covering
+    block of ``blockmask`` ([ceil(n_q / mb), ceil(n_k / mb)]) is zero.  Both may
+    apply; a key is visible iff both allow.
     """
     allowed = np.ones((n_q, n_k), dtype=bool)
     if causal:
-        allowed &= np.arange(n_k)[None, :] <= np.arange(n_q)[:, None]
+        allowed &= np.arange(n_k)[None, :] <= np.arange(n_q)[:, None] + (n_k - n_q)
     if blockmask is not None:
         bm = np.asarray(blockmask).astype(bool)
         bi = np.arange(n_q) // mask_block
