@@ -51,6 +51,9 @@ _SIGNATURES = {
     "fa_bwd_dropout": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i,
                             _f, _u64, _u32, _vp, _vp, _vp, _vp, _sz, _vp]),
     "fa_dropout_keep_mask": (_i, [_i, _i, _i, _f, _u64, _u32, _vp, _vp]),
+    "fa_fwd_nqk": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _i, _vp, _vp, _vp]),
+    "fa_bwd_nqk": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _i,
+                        _vp, _vp, _vp, _vp, _sz, _vp]),
     "fa_strerror": (ctypes.c_char_p, [_i]),
 }
 
@@ -119,12 +122,13 @@ def _check(t, name, dtype, shape=None, device=None):
         raise ValueError(f"{name} is on {t.device}, expected {device}")
 
 
-def _mask_args(blockmask, N, mask_block, device):
+def _mask_args(blockmask, N, mask_block, device, Nk=None):
     torch = _torch()
     if blockmask is None:
         return None, 0
     nb = -(-N // mask_block)
-    _check(blockmask, "blockmask", torch.uint8, (nb, nb), device)
+    nbk = nb if Nk is None else -(-Nk // mask_block)
+    _check(blockmask, "blockmask", torch.uint8, (nb, nbk), device)
     return blockmask.data_ptr(), mask_block
 
 
@@ -142,16 +146,23 @@ def forward(q, k, v, scale: float | None = None, causal: bool = False, blockmask
             offset: int = 0):
     """O, LSE = attention forward.  Returns (o [B,H,N,d] bf16, lse [B,H,N] fp32).
 
-    dropout_p > 0 runs fa_fwd_dropout with that (p, seed, offset); pass the same
-    three to ``backward``."""
+    k and v may have another sequence length Nk than q (fa_fwd_nqk; the causal
+    mask is then aligned bottom-right).  dropout_p > 0 runs fa_fwd_dropout with
+    that (p, seed, offset); pass the same three to ``backward``."""
     torch = _torch()
     _check(q, "q", torch.bfloat16)
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
     B, H, N, d = q.shape
     dev = q.device
-    _check(k, "k", torch.bfloat16, q.shape, dev)
-    _check(v, "v", torch.bfloat16, q.shape, dev)
+    if k.dim() != 4:
+        raise ValueError("k must be [B, H, Nk, d]")
+    Nk = k.shape[2]
+    kshape = (B, H, Nk, d)
+    _check(k, "k", torch.bfloat16, kshape, dev)
+    _check(v, "v", torch.bfloat16, kshape, dev)
+    if Nk != N and dropout_p:
+        raise ValueError("dropout is supported with equal query and key lengths only")
     scale = default_scale(d) if scale is None else float(scale)
     if out is None:
         out = torch.empty_like(q)
@@ -161,7 +172,7 @@ def forward(q, k, v, scale: float | None = None, causal: bool = False, blockmask
         lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
     else:
         _check(lse, "lse", torch.float32, (B, H, N), dev)
-    bm_ptr, mb = _mask_args(blockmask, N, mask_block, dev)
+    bm_ptr, mb = _mask_args(blockmask, N, mask_block, dev, Nk)
     if dropout_p:
         rc = load_library().fa_fwd_dropout(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, d,
                                            scale, int(bool(causal)), bm_ptr, mb,
@@ -169,6 +180,13 @@ def forward(q, k, v, scale: float | None = None, causal: bool = False, blockmask
                                            out.data_ptr(), lse.data_ptr(), _stream_ptr(dev))
         if rc != FA_OK:
             raise LibfaError(rc, "fa_fwd_dropout")
+        return out, lse
+    if Nk != N:
+        rc = load_library().fa_fwd_nqk(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, Nk, d,
+                                       scale, int(bool(causal)), bm_ptr, mb, out.data_ptr(),
+                                       lse.data_ptr(), _stream_ptr(dev))
+        if rc != FA_OK:
+            raise LibfaError(rc, "fa_fwd_nqk")
         return out, lse
     rc = load_library().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, d, scale,
                                int(bool(causal)), bm_ptr, mb, out.data_ptr(), lse.data_ptr(),
@@ -181,35 +199,50 @@ def forward(q, k, v, scale: float | None = None, causal: bool = False, blockmask
 def backward(q, k, v, o, do, lse, scale: float | None = None, causal: bool = False,
              blockmask=None, mask_block: int = 128, workspace=None, dq=None, dk=None, dv=None,
              dropout_p: float = 0.0, seed: int = 0, offset: int = 0):
-    """dQ, dK, dV of sum(dO * O).  Returns three [B,H,N,d] bf16 tensors.
+    """dQ, dK, dV of sum(dO * O).  Returns (dq [B,H,N,d], dk, dv [B,H,Nk,d]) bf16.
 
-    dropout_p > 0 runs fa_bwd_dropout (the forward must have used the same
-    dropout_p, seed and offset)."""
+    k and v may have another length Nk than q (fa_bwd_nqk).  dropout_p > 0 runs
+    fa_bwd_dropout (the forward must have used the same dropout_p, seed and
+    offset)."""
     torch = _torch()
     _check(q, "q", torch.bfloat16)
     if q.dim() != 4:
         raise ValueError("q must be [B, H, N, d]")
     B, H, N, d = q.shape
     dev = q.device
-    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
-        _check(t, name, torch.bfloat16, q.shape, dev)
+    if k.dim() != 4:
+        raise ValueError("k must be [B, H, Nk, d]")
+    Nk = k.shape[2]
+    kshape = (B, H, Nk, d)
+    for name, t, shape in (("k", k, kshape), ("v", v, kshape), ("o", o, q.shape),
+                           ("do", do, q.shape)):
+        _check(t, name, torch.bfloat16, shape, dev)
     _check(lse, "lse", torch.float32, (B, H, N), dev)
+    if Nk != N and dropout_p:
+        raise ValueError("dropout is supported with equal query and key lengths only")
     scale = default_scale(d) if scale is None else float(scale)
     outs = []
-    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+    for name, t, shape in (("dq", dq, q.shape), ("dk", dk, kshape), ("dv", dv, kshape)):
         if t is None:
-            t = torch.empty_like(q)
+            t = torch.empty(shape, dtype=torch.bfloat16, device=dev)
         else:
-            _check(t, name, torch.bfloat16, q.shape, dev)
+            _check(t, name, torch.bfloat16, shape, dev)
         outs.append(t)
     nbytes = bwd_workspace_bytes(B, H, N, d) if d in (64, 128) else 0
     if workspace is None:
         workspace = torch.empty(max(nbytes, 4), dtype=torch.uint8, device=dev)
-    bm_ptr, mb = _mask_args(blockmask, N, mask_block, dev)
+    bm_ptr, mb = _mask_args(blockmask, N, mask_block, dev, Nk)
     ws = (workspace.data_ptr(), workspace.numel() * workspace.element_size(), _stream_ptr(dev))
+    grads = (outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr())
+    if Nk != N:
+        rc = load_library().fa_bwd_nqk(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                       do.data_ptr(), lse.data_ptr(), B, H, N, Nk, d, scale,
+                                       int(bool(causal)), bm_ptr, mb, *grads, *ws)
+        if rc != FA_OK:
+            raise LibfaError(rc, "fa_bwd_nqk")
+        return tuple(outs)
     ptrs = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), do.data_ptr(),
             lse.data_ptr(), B, H, N, d, scale, int(bool(causal)), bm_ptr, mb)
-    grads = (outs[0].data_ptr(), outs[1].data_ptr(), outs[2].data_ptr())
     if dropout_p:
         rc = load_library().fa_bwd_dropout(*ptrs, float(dropout_p), int(seed), int(offset),
                                            *grads, *ws)

@@ -19,27 +19,39 @@ constexpr long long kMaxI32 = 2147483647LL;
 
 bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// Shapes only.  Sets *empty when there is nothing to compute.
-int check_shape(int B, int H, int N, int d, bool* empty) {
-  if (B < 0 || H < 0 || N < 0 || d < 0) return FA_ERR_SHAPE;
+// Shapes only (Nq query rows, Nk key rows).  Sets *empty when there is
+// nothing to compute (no query rows).
+int check_shape(int B, int H, int Nq, int Nk, int d, bool* empty) {
+  if (B < 0 || H < 0 || Nq < 0 || Nk < 0 || d < 0) return FA_ERR_SHAPE;
   if (d != 64 && d != 128) return FA_ERR_UNSUPPORTED;
-  if ((long long)N * d > kMaxI32) return FA_ERR_UNSUPPORTED;
-  const long long nqb = ((long long)N + 127) / 128;
-  if (nqb * B * H > kMaxI32) return FA_ERR_UNSUPPORTED;
-  if ((long long)B * H * N > kMaxI32) return FA_ERR_UNSUPPORTED;
-  *empty = (long long)B * H * N == 0;
+  for (const int n : {Nq, Nk}) {
+    if ((long long)n * d > kMaxI32) return FA_ERR_UNSUPPORTED;
+    const long long nb = ((long long)n + 127) / 128;
+    if (nb * B * H > kMaxI32) return FA_ERR_UNSUPPORTED;
+    if ((long long)B * H * n > kMaxI32) return FA_ERR_UNSUPPORTED;
+  }
+  *empty = (long long)B * H * Nq == 0;
   return FA_OK;
 }
 
+int check_shape(int B, int H, int N, int d, bool* empty) {
+  return check_shape(B, H, N, N, d, empty);
+}
+
 // Shapes, scale and mask arguments.
-int check_common(int B, int H, int N, int d, float scale, const uint8_t* blockmask,
+int check_common(int B, int H, int Nq, int Nk, int d, float scale, const uint8_t* blockmask,
                  int mask_block, bool* empty) {
-  const int rc = check_shape(B, H, N, d, empty);
+  const int rc = check_shape(B, H, Nq, Nk, d, empty);
   if (rc != FA_OK) return rc;
   if (!std::isfinite(scale) || !(scale > 0.f)) return FA_ERR_UNSUPPORTED;
   if (blockmask != nullptr && (mask_block <= 0 || mask_block % 128 != 0))
     return FA_ERR_UNSUPPORTED;
   return FA_OK;
+}
+
+int check_common(int B, int H, int N, int d, float scale, const uint8_t* blockmask,
+                 int mask_block, bool* empty) {
+  return check_common(B, H, N, N, d, scale, blockmask, mask_block, empty);
 }
 
 bool all_aligned16(std::initializer_list<const void*> ps) {
@@ -49,8 +61,8 @@ bool all_aligned16(std::initializer_list<const void*> ps) {
 }
 
 fa::BwdParams bwd_params(const void* Q, const void* K, const void* V, const void* O,
-                         const void* dO, const float* LSE, float* Dsum, int B, int H, int N,
-                         float scale, const uint8_t* blockmask, int mask_block, void* dQ,
+                         const void* dO, const float* LSE, float* Dsum, int B, int H, int Nq,
+                         int Nk, float scale, const uint8_t* blockmask, int mask_block, void* dQ,
                          void* dK, void* dV) {
   fa::BwdParams p;
   p.Q = static_cast<const uint16_t*>(Q);
@@ -65,14 +77,26 @@ fa::BwdParams bwd_params(const void* Q, const void* K, const void* V, const void
   p.dV = static_cast<uint16_t*>(dV);
   p.blockmask = blockmask;
   p.BH = B * H;
-  p.N = N;
-  p.nqb = (N + 127) / 128;
-  p.nkb = (N + 127) / 128;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.nqb = (Nq + 127) / 128;
+  p.nkb = (Nk + 127) / 128;
   p.mask_block = blockmask ? mask_block : 128;
-  p.nbm = (N + p.mask_block - 1) / p.mask_block;
+  p.nbm = (Nk + p.mask_block - 1) / p.mask_block;
   p.scale = scale;
   p.scale_log2 = scale * kLog2e;
+  p.drop_thresh = 0;
+  p.drop_scale = 1.f;
+  p.seed_lo = p.seed_hi = p.drop_offset = 0;
   return p;
+}
+
+fa::BwdParams bwd_params(const void* Q, const void* K, const void* V, const void* O,
+                         const void* dO, const float* LSE, float* Dsum, int B, int H, int N,
+                         float scale, const uint8_t* blockmask, int mask_block, void* dQ,
+                         void* dK, void* dV) {
+  return bwd_params(Q, K, V, O, dO, LSE, Dsum, B, H, N, N, scale, blockmask, mask_block, dQ, dK,
+                    dV);
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? FA_OK : FA_ERR_HIP; }
@@ -95,16 +119,17 @@ void set_dropout(Params& p, float p_drop, uint64_t seed, uint32_t offset) {
   p.drop_offset = offset;
 }
 
-int fwd_impl(const void* Q, const void* K, const void* V, int B, int H, int N, int d,
+int fwd_impl(const void* Q, const void* K, const void* V, int B, int H, int Nq, int Nk, int d,
              float scale, int causal, const uint8_t* blockmask, int mask_block, float p_drop,
              uint64_t seed, uint32_t offset, void* O, float* LSE, hipStream_t stream) {
   bool empty = false;
-  int rc = check_common(B, H, N, d, scale, blockmask, mask_block, &empty);
+  int rc = check_common(B, H, Nq, Nk, d, scale, blockmask, mask_block, &empty);
   if (rc != FA_OK) return rc;
   rc = check_dropout(p_drop);
   if (rc != FA_OK) return rc;
   if (empty) return FA_OK;
-  if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
+  if (!Q || !O || !LSE) return FA_ERR_NULL;
+  if ((long long)B * H * Nk > 0 && (!K || !V)) return FA_ERR_NULL;   // no keys: O = 0
   if (!all_aligned16({Q, K, V, O}) || !aligned(LSE, 4)) return FA_ERR_UNSUPPORTED;
 
   fa::FwdParams p;
@@ -115,10 +140,11 @@ int fwd_impl(const void* Q, const void* K, const void* V, int B, int H, int N, i
   p.LSE = LSE;
   p.blockmask = blockmask;
   p.BH = B * H;
-  p.N = N;
-  p.nqb = (N + 127) / 128;
+  p.Nq = Nq;
+  p.Nk = Nk;
+  p.nqb = (Nq + 127) / 128;
   p.mask_block = blockmask ? mask_block : 128;
-  p.nbm = (N + p.mask_block - 1) / p.mask_block;
+  p.nbm = (Nk + p.mask_block - 1) / p.mask_block;
   p.scale_log2 = scale * kLog2e;
   set_dropout(p, p_drop, seed, offset);
   return status_of(
@@ -126,7 +152,7 @@ int fwd_impl(const void* Q, const void* K, const void* V, int B, int H, int N, i
 }
 
 int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-             const float* LSE, int B, int H, int N, int d, float scale, int causal,
+             const float* LSE, int B, int H, int Nq, int Nk, int d, float scale, int causal,
              const uint8_t* blockmask, int mask_block, float p_drop, uint64_t seed,
              uint32_t offset, void* dQ, void* dK, void* dV, void* workspace,
              size_t workspace_bytes, hipStream_t stream);
@@ -152,15 +178,22 @@ const char* fa_strerror(int status) {
 int fa_fwd(const void* Q, const void* K, const void* V, int B, int H, int N, int d, float scale,
            int causal, const uint8_t* blockmask, int mask_block, void* O, float* LSE,
            hipStream_t stream) {
-  return fwd_impl(Q, K, V, B, H, N, d, scale, causal, blockmask, mask_block, 0.f, 0, 0, O, LSE,
-                  stream);
+  return fwd_impl(Q, K, V, B, H, N, N, d, scale, causal, blockmask, mask_block, 0.f, 0, 0, O,
+                  LSE, stream);
+}
+
+int fa_fwd_nqk(const void* Q, const void* K, const void* V, int B, int H, int Nq, int Nk, int d,
+               float scale, int causal, const uint8_t* blockmask, int mask_block, void* O,
+               float* LSE, hipStream_t stream) {
+  return fwd_impl(Q, K, V, B, H, Nq, Nk, d, scale, causal, blockmask, mask_block, 0.f, 0, 0, O,
+                  LSE, stream);
 }
 
 int fa_fwd_dropout(const void* Q, const void* K, const void* V, int B, int H, int N, int d,
                    float scale, int causal, const uint8_t* blockmask, int mask_block,
                    float p_drop, uint64_t seed, uint32_t offset, void* O, float* LSE,
                    hipStream_t stream) {
-  return fwd_impl(Q, K, V, B, H, N, d, scale, causal, blockmask, mask_block, p_drop, seed,
+  return fwd_impl(Q, K, V, B, H, N, N, d, scale, causal, blockmask, mask_block, p_drop, seed,
                   offset, O, LSE, stream);
 }
 
@@ -236,8 +269,16 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
            const float* LSE, int B, int H, int N, int d, float scale, int causal,
            const uint8_t* blockmask, int mask_block, void* dQ, void* dK, void* dV,
            void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return bwd_impl(Q, K, V, O, dO, LSE, B, H, N, d, scale, causal, blockmask, mask_block, 0.f, 0,
-                  0, dQ, dK, dV, workspace, workspace_bytes, stream);
+  return bwd_impl(Q, K, V, O, dO, LSE, B, H, N, N, d, scale, causal, blockmask, mask_block, 0.f,
+                  0, 0, dQ, dK, dV, workspace, workspace_bytes, stream);
+}
+
+int fa_bwd_nqk(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+               const float* LSE, int B, int H, int Nq, int Nk, int d, float scale, int causal,
+               const uint8_t* blockmask, int mask_block, void* dQ, void* dK, void* dV,
+               void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return bwd_impl(Q, K, V, O, dO, LSE, B, H, Nq, Nk, d, scale, causal, blockmask, mask_block,
+                  0.f, 0, 0, dQ, dK, dV, workspace, workspace_bytes, stream);
 }
 
 int fa_bwd_dropout(const void* Q, const void* K, const void* V, const void* O, const void* dO,
@@ -245,8 +286,8 @@ int fa_bwd_dropout(const void* Q, const void* K, const void* V, const void* O, c
                    const uint8_t* blockmask, int mask_block, float p_drop, uint64_t seed,
                    uint32_t offset, void* dQ, void* dK, void* dV, void* workspace,
                    size_t workspace_bytes, hipStream_t stream) {
-  return bwd_impl(Q, K, V, O, dO, LSE, B, H, N, d, scale, causal, blockmask, mask_block, p_drop,
-                  seed, offset, dQ, dK, dV, workspace, workspace_bytes, stream);
+  return bwd_impl(Q, K, V, O, dO, LSE, B, H, N, N, d, scale, causal, blockmask, mask_block,
+                  p_drop, seed, offset, dQ, dK, dV, workspace, workspace_bytes, stream);
 }
 
 int fa_dropout_keep_mask(int B, int H, int N, float p_drop, uint64_t seed, uint32_t offset,
@@ -259,7 +300,8 @@ int fa_dropout_keep_mask(int B, int H, int N, float p_drop, uint64_t seed, uint3
   if (!keep) return FA_ERR_NULL;
   fa::FwdParams p{};
   p.BH = B * H;
-  p.N = N;
+  p.Nq = N;
+  p.Nk = N;
   set_dropout(p, p_drop, seed, offset);
   return status_of(fa::launch_dropout_keep_mask(p, keep, stream));
 }
@@ -269,28 +311,31 @@ int fa_dropout_keep_mask(int B, int H, int N, float p_drop, uint64_t seed, uint3
 namespace {
 
 int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const void* dO,
-             const float* LSE, int B, int H, int N, int d, float scale, int causal,
+             const float* LSE, int B, int H, int Nq, int Nk, int d, float scale, int causal,
              const uint8_t* blockmask, int mask_block, float p_drop, uint64_t seed,
              uint32_t offset, void* dQ, void* dK, void* dV, void* workspace,
              size_t workspace_bytes, hipStream_t stream) {
   bool empty = false;
-  int rc = check_common(B, H, N, d, scale, blockmask, mask_block, &empty);
+  int rc = check_common(B, H, Nq, Nk, d, scale, blockmask, mask_block, &empty);
   if (rc != FA_OK) return rc;
   rc = check_dropout(p_drop);
   if (rc != FA_OK) return rc;
-  if (empty) return FA_OK;
-  if (!Q || !K || !V || !O || !dO || !LSE || !dQ || !dK || !dV) return FA_ERR_NULL;
-  if (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, N, d))
+  // no query rows: dK = dV = 0 still has to be written when there are keys
+  const bool no_keys = (long long)B * H * Nk == 0;
+  if (empty && no_keys) return FA_OK;
+  if (!empty && (!Q || !O || !dO || !LSE || !dQ)) return FA_ERR_NULL;
+  if (!no_keys && (!K || !V || !dK || !dV)) return FA_ERR_NULL;
+  if (!empty && (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, Nq, d)))
     return FA_ERR_WORKSPACE;
   if (!all_aligned16({Q, K, V, O, dO, dQ, dK, dV}) || !aligned(LSE, 4) || !aligned(workspace, 4))
     return FA_ERR_UNSUPPORTED;
-  fa::BwdParams p = bwd_params(Q, K, V, O, dO, LSE, static_cast<float*>(workspace), B, H, N,
-                               scale, blockmask, mask_block, dQ, dK, dV);
+  fa::BwdParams p = bwd_params(Q, K, V, O, dO, LSE, static_cast<float*>(workspace), B, H, Nq,
+                               Nk, scale, blockmask, mask_block, dQ, dK, dV);
   set_dropout(p, p_drop, seed, offset);
   const bool cz = causal != 0, sp = blockmask != nullptr, dr = p_drop > 0.f;
   // dQ first, forming D on the way (the same bits fa_bwd_dsum writes), then dK, dV
-  rc = status_of(fa::launch_bwd_dq(p, d, cz, sp, true, dr, stream));
-  if (rc == FA_OK) rc = status_of(fa::launch_bwd_dkdv(p, d, cz, sp, dr, stream));
+  if (!empty) rc = status_of(fa::launch_bwd_dq(p, d, cz, sp, true, dr, stream));
+  if (rc == FA_OK && !no_keys) rc = status_of(fa::launch_bwd_dkdv(p, d, cz, sp, dr, stream));
   return rc;
 }
 

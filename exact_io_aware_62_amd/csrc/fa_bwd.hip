@@ -100,26 +100,27 @@ __global__ __launch_bounds__(256, (DROPOUT && D == 128) ? 1 : 2) void dkdv_kerne
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const BlockCoord bc = block_coord(p.nkb);
   const int kb = bc.blk;
-  const int N = p.N;
-  const size_t head = (size_t)bc.bh * N * D;
-  const uint16_t* __restrict__ Qh = p.Q + head;
-  const uint16_t* __restrict__ dOh = p.dO + head;
-  const float* __restrict__ lseh = p.LSE + (size_t)bc.bh * N;
-  const float* __restrict__ Dh = p.Dsum + (size_t)bc.bh * N;
+  // Nq queries, Nk keys; causal: query i sees key j iff j <= i + dlt
+  const int Nq = p.Nq, Nk = p.Nk, dlt = Nk - Nq;
+  const size_t qhead = (size_t)bc.bh * Nq * D, khead = (size_t)bc.bh * Nk * D;
+  const uint16_t* __restrict__ Qh = p.Q + qhead;
+  const uint16_t* __restrict__ dOh = p.dO + qhead;
+  const float* __restrict__ lseh = p.LSE + (size_t)bc.bh * Nq;
+  const float* __restrict__ Dh = p.Dsum + (size_t)bc.bh * Nq;
 
   const int kw = kb * BKB + wave * 32;   // first key of this wavefront
   const int key = kw + r;                // this lane's key
-  copy_async<TK, NW>(p.K + head, kb * BKB, N, lds_addr(kbuf), wave,
+  copy_async<TK, NW>(p.K + khead, kb * BKB, Nk, lds_addr(kbuf), wave,
                      TK::template lane_offsets<NW>(wave, lane));
   bf16x8 vf[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk)
-    vf[kk] = as_bf16x8(key < N ? ldg16(p.V + head + (size_t)key * D + kk * 16 + g * 8)
-                               : zero_u32x4());
+    vf[kk] = as_bf16x8(key < Nk ? ldg16(p.V + khead + (size_t)key * D + kk * 16 + g * 8)
+                                : zero_u32x4());
 
-  // query tiles: causal => only rows >= first key of the block
-  const int nqt = (N + BQ - 1) / BQ;
-  const int t_begin = CAUSAL ? (kb * BKB) / BQ : 0;
+  // query tiles: causal => only rows i >= (first key of the block) - dlt
+  const int nqt = (Nq + BQ - 1) / BQ;
+  const int t_begin = CAUSAL ? max(0, kb * BKB - dlt) / BQ : 0;
   const int mcol = SPARSE ? (kb * BKB) / p.mask_block : 0;
   auto next_tile = [&](int t) FA_INLINE -> int {
     if constexpr (SPARSE) {
@@ -160,18 +161,18 @@ __global__ __launch_bounds__(256, (DROPOUT && D == 128) ? 1 : 2) void dkdv_kerne
   auto issue = [&](int t, int bufi) FA_INLINE {
     if (tid < 2 * BQ) {
       rowq = t * BQ + (tid % BQ);
-      const int qc = min(rowq, N - 1);
+      const int qc = min(rowq, Nq - 1);
       rowv = tid < BQ ? lseh[qc] : Dh[qc];
     }
-    copy_async<TQ, NW>(Qh, t * BQ, N, lds_addr(qbuf) + bufi * TQ::kBytes, wave, lofs);
-    copy_async<TQ, NW>(dOh, t * BQ, N, lds_addr(obuf) + bufi * TQ::kBytes, wave, lofs);
+    copy_async<TQ, NW>(Qh, t * BQ, Nq, lds_addr(qbuf) + bufi * TQ::kBytes, wave, lofs);
+    copy_async<TQ, NW>(dOh, t * BQ, Nq, lds_addr(obuf) + bufi * TQ::kBytes, wave, lofs);
   };
   auto finish_issue = [&](int bufi) FA_INLINE {
     __builtin_amdgcn_sched_barrier(0);
     if (tid < 2 * BQ) {
       float v;
-      if (tid < BQ) v = rowq < N ? lse_to_log2(rowv) : INFINITY;
-      else v = rowq < N ? rowv : 0.f;
+      if (tid < BQ) v = rowq < Nq ? lse_to_log2(rowv) : INFINITY;
+      else v = rowq < Nq ? rowv : 0.f;
       rowbuf[bufi * 2 * BQ + tid] = v;
     }
   };
@@ -247,7 +248,7 @@ __global__ __launch_bounds__(256, (DROPOUT && D == 128) ? 1 : 2) void dkdv_kerne
     }
 
     // mask: causal diagonal, ragged query or key ends (rare tiles only)
-    const bool need_mask = (CAUSAL && q0 < kw + 31) || (q0 + BQ > N) || (kw + 32 > N);
+    const bool need_mask = (CAUSAL && q0 + dlt < kw + 31) || (q0 + BQ > Nq) || (kw + 32 > Nk);
     if (need_mask) {
       // register i holds query q0 + (i/4)*8 + g*4 + i%4; this lane's key
       const int ln = lane_id();
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(256, (DROPOUT && D == 128) ? 1 : 2) void dkdv_kerne
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int q = qg + (i >> 2) * 8 + (i & 3);
-        if ((CAUSAL && kl > q) || q >= N || kl >= N) s[i] = -INFINITY;
+        if ((CAUSAL && kl > q + dlt) || q >= Nq || kl >= Nk) s[i] = -INFINITY;
       }
     }
 
@@ -349,9 +350,9 @@ __global__ __launch_bounds__(256, (DROPOUT && D == 128) ? 1 : 2) void dkdv_kerne
 
   // epilogue: lane owns key `key`; register i of block db is column
   // db*32 + (i/4)*8 + g*4 + i%4
-  if (key < N) {
-    uint16_t* dKh = p.dK + head + (size_t)key * D;
-    uint16_t* dVh = p.dV + head + (size_t)key * D;
+  if (key < Nk) {
+    uint16_t* dKh = p.dK + khead + (size_t)key * D;
+    uint16_t* dVh = p.dV + khead + (size_t)key * D;
     const float sc = p.scale;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -409,10 +410,11 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const BlockCoord bc = block_coord(p.nqb);
   const int qb = CAUSAL ? (p.nqb - 1 - bc.blk) : bc.blk;
-  const int N = p.N;
-  const size_t head = (size_t)bc.bh * N * D;
-  const uint16_t* __restrict__ Kh = p.K + head;
-  const uint16_t* __restrict__ Vh = p.V + head;
+  // Nq queries, Nk keys; causal: query i sees key j iff j <= i + dlt
+  const int Nq = p.Nq, Nk = p.Nk, dlt = Nk - Nq;
+  const size_t qhead = (size_t)bc.bh * Nq * D, khead = (size_t)bc.bh * Nk * D;
+  const uint16_t* __restrict__ Kh = p.K + khead;
+  const uint16_t* __restrict__ Vh = p.V + khead;
 
   const int q0w = qb * BQ + wave * 32;
   const int qrow = q0w + r;
@@ -420,18 +422,18 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk) {
     const size_t off = (size_t)qrow * D + kk * 16 + g * 8;
-    qf[kk] = as_bf16x8(qrow < N ? ldg16(p.Q + head + off) : zero_u32x4());
-    of[kk] = as_bf16x8(qrow < N ? ldg16(p.dO + head + off) : zero_u32x4());
+    qf[kk] = as_bf16x8(qrow < Nq ? ldg16(p.Q + qhead + off) : zero_u32x4());
+    of[kk] = as_bf16x8(qrow < Nq ? ldg16(p.dO + qhead + off) : zero_u32x4());
   }
-  const float lse2 = qrow < N ? lse_to_log2(p.LSE[(size_t)bc.bh * N + qrow]) : INFINITY;
+  const float lse2 = qrow < Nq ? lse_to_log2(p.LSE[(size_t)bc.bh * Nq + qrow]) : INFINITY;
   float dsum;
   if constexpr (FUSED_D) {
     // chunk c = 2 kk + g of the row (columns 8c .. 8c+7) is in of[kk]
     float part[NKK];
 #pragma unroll
     for (int kk = 0; kk < NKK; ++kk) {
-      const u32x4 o = qrow < N ? ldg16(p.O + head + (size_t)qrow * D + kk * 16 + g * 8)
-                               : zero_u32x4();
+      const u32x4 o = qrow < Nq ? ldg16(p.O + qhead + (size_t)qrow * D + kk * 16 + g * 8)
+                                : zero_u32x4();
       const u32x4 gd = __builtin_bit_cast(u32x4, of[kk]);
       float acc = 0.f;
 #pragma unroll
@@ -450,12 +452,12 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
       for (int kk = 0; kk < NKK; ++kk)
         if (!(kk & off)) part[kk] = part[kk] + part[kk | off];
     dsum = sum_xor32(part[0]);
-    if (g == 0 && qrow < N) p.Dsum[(size_t)bc.bh * N + qrow] = dsum;
+    if (g == 0 && qrow < Nq) p.Dsum[(size_t)bc.bh * Nq + qrow] = dsum;
   } else {
-    dsum = qrow < N ? p.Dsum[(size_t)bc.bh * N + qrow] : 0.f;
+    dsum = qrow < Nq ? p.Dsum[(size_t)bc.bh * Nq + qrow] : 0.f;
   }
 
-  const int kend = CAUSAL ? min(N, (qb + 1) * BQ) : N;
+  const int kend = CAUSAL ? max(0, min(Nk, (qb + 1) * BQ + dlt)) : Nk;
   const int ntiles = (kend + BK - 1) / BK;
   const int mrow = SPARSE ? (qb * BQ) / p.mask_block : 0;
   auto next_tile = [&](int t) FA_INLINE -> int {
@@ -481,8 +483,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
 
   const auto lofs = T::template lane_offsets<NW>(wave, lane);
   auto issue = [&](int t, int stage) FA_INLINE {
-    copy_async<T, NW>(Kh, t * BK, N, lds_addr(kbuf) + stage * T::kBytes, wave, lofs);
-    copy_async<T, NW>(Vh, t * BK, N, lds_addr(vbuf) + stage * T::kBytes, wave, lofs);
+    copy_async<T, NW>(Kh, t * BK, Nk, lds_addr(kbuf) + stage * T::kBytes, wave, lofs);
+    copy_async<T, NW>(Vh, t * BK, Nk, lds_addr(vbuf) + stage * T::kBytes, wave, lofs);
   };
 
   const OperandAddr<T> oa = operand_addr<T>(lane);
@@ -505,7 +507,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     const char* kt = kbuf + stage * T::kBytes;
     const char* vt = vbuf + stage * T::kBytes;
     const int k0 = t * BK;
-    const bool need_mask = (CAUSAL && k0 + BK - 1 > q0w) || (k0 + BK > N);
+    const bool need_mask = (CAUSAL && k0 + BK - 1 > q0w + dlt) || (k0 + BK > Nk);
     f32x16 s[2], dp[2];
     bf16x8 ds[4];   // dS^T B operands, entry kb * 2 + ks2
     s[0] = zero16(); s[1] = zero16(); dp[0] = zero16(); dp[1] = zero16();
@@ -550,7 +552,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
               // register i holds key k0 + kb*32 + (i/4)*8 + g*4 + i%4
               const int ln = lane_id();
               const int kl = k0 + kb * 32 + (ln >> 5) * 4;
-              const int lim = CAUSAL ? min(N - 1, q0w + (ln & 31)) - kl : N - 1 - kl;
+              const int lim = CAUSAL ? min(Nk - 1, q0w + (ln & 31) + dlt) - kl : Nk - 1 - kl;
 #pragma unroll
               for (int i = 0; i < 16; ++i)
                 if ((i >> 2) * 8 + (i & 3) > lim) s[kb][i] = -INFINITY;
@@ -592,13 +594,13 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     const int tn = next_tile(t + 1);
     if (tn < ntiles) issue(tn, stage ^ 1);
     // a tile entirely above this wavefront's causal diagonal contributes 0
-    if (!(CAUSAL && t * BK > q0w + 31)) compute(stage, t);
+    if (!(CAUSAL && t * BK > q0w + 31 + dlt)) compute(stage, t);
     t = tn;
     stage ^= 1;
   }
 
-  if (qrow < N) {
-    uint16_t* dQh = p.dQ + head + (size_t)qrow * D;
+  if (qrow < Nq) {
+    uint16_t* dQh = p.dQ + qhead + (size_t)qrow * D;
     const float sc = p.scale;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
@@ -611,7 +613,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
 }
 
 hipError_t launch_bwd_dsum(const BwdParams& p, int d, hipStream_t stream) {
-  const long long rows = (long long)p.BH * p.N;
+  const long long rows = (long long)p.BH * p.Nq;
   if (d == 64) {
     constexpr int RPB = 256 / (64 / 8);
     hipLaunchKernelGGL((dsum_kernel<64>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,

@@ -71,11 +71,13 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const BlockCoord bc = block_coord(p.nqb);
   // heaviest query blocks first under the causal mask
   const int qb = CAUSAL ? (p.nqb - 1 - bc.blk) : bc.blk;
-  const int N = p.N;
-  const size_t head = (size_t)bc.bh * N * D;
-  const uint16_t* __restrict__ Qh = p.Q + head;
-  const uint16_t* __restrict__ Kh = p.K + head;
-  const uint16_t* __restrict__ Vh = p.V + head;
+  // Nq queries, Nk keys; under the causal mask query i sees key j iff
+  // j <= i + dlt (the queries are the last Nq positions of the key sequence)
+  const int Nq = p.Nq, Nk = p.Nk, dlt = Nk - Nq;
+  const size_t qhead = (size_t)bc.bh * Nq * D, khead = (size_t)bc.bh * Nk * D;
+  const uint16_t* __restrict__ Qh = p.Q + qhead;
+  const uint16_t* __restrict__ Kh = p.K + khead;
+  const uint16_t* __restrict__ Vh = p.V + khead;
 
   const int q0w = qb * BQ + wave * 32;   // first query row of this wavefront
   const int qrow = q0w + r;              // this lane's query row
@@ -84,11 +86,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   bf16x8 qf[NKK];
 #pragma unroll
   for (int kk = 0; kk < NKK; ++kk)
-    qf[kk] = as_bf16x8(qrow < N ? ldg16(Qh + (size_t)qrow * D + kk * 16 + g * 8)
-                                : zero_u32x4());
+    qf[kk] = as_bf16x8(qrow < Nq ? ldg16(Qh + (size_t)qrow * D + kk * 16 + g * 8)
+                                 : zero_u32x4());
 
   // key range and tile schedule
-  const int kend = CAUSAL ? min(N, (qb + 1) * BQ) : N;
+  const int kend = CAUSAL ? max(0, min(Nk, (qb + 1) * BQ + dlt)) : Nk;
   const int ntiles = (kend + BK - 1) / BK;
   const int mrow = SPARSE ? (qb * BQ) / p.mask_block : 0;
   auto next_tile = [&](int t) FA_INLINE -> int {
@@ -100,7 +102,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   };
   // wavefront-uniform tile predicates
   auto needs_mask = [&](int t) FA_INLINE {
-    return (CAUSAL && t * BK + BK - 1 > q0w) || (t * BK + BK > N);
+    return (CAUSAL && t * BK + BK - 1 > q0w + dlt) || (t * BK + BK > Nk);
   };
 
   f32x16 oacc[NDB];
@@ -134,10 +136,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 
   const auto lofs = T::template lane_offsets<NW>(wave, lane);
   auto load_k = [&](int t, int buf) FA_INLINE {
-    T::template copy<NW>(Kh, t * BK, N, buf ? kbuf1 : kbuf0, wave, lofs);
+    T::template copy<NW>(Kh, t * BK, Nk, buf ? kbuf1 : kbuf0, wave, lofs);
   };
   auto load_v = [&](int t, int buf) FA_INLINE {
-    T::template copy<NW>(Vh, t * BK, N, buf ? vbuf1 : vbuf0, wave, lofs);
+    T::template copy<NW>(Vh, t * BK, Nk, buf ? vbuf1 : vbuf0, wave, lofs);
   };
 
   // P = exp2(S c - m), packed to the bf16 B operands of the PV product:
@@ -182,7 +184,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       // lane id recomputed here (two vector ops) rather than kept live
       const int ln = lane_id();
       const int kl = tc * BK + (ln >> 5) * 4;
-      const int lim = CAUSAL ? min(N - 1, q0w + (ln & 31)) - kl : N - 1 - kl;
+      const int lim = CAUSAL ? min(Nk - 1, q0w + (ln & 31) + dlt) - kl : Nk - 1 - kl;
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -393,8 +395,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   // epilogue: combine the two lane halves' partial sums, divide once
   const float l_tot = sum_xor32(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-  if (qrow < N) {
-    uint16_t* Oh = p.O + head + (size_t)qrow * D;
+  if (qrow < Nq) {
+    uint16_t* Oh = p.O + qhead + (size_t)qrow * D;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll
@@ -404,7 +406,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
         *reinterpret_cast<u32x2*>(Oh + db * 32 + qd * 8 + g * 4) = v;
       }
     if (g == 0)
-      p.LSE[(size_t)bc.bh * N + qrow] =
+      p.LSE[(size_t)bc.bh * Nq + qrow] =
           l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
@@ -439,10 +441,10 @@ __global__ __launch_bounds__(256) void dropout_keep_mask_kernel(FwdParams p, uin
                                                                long long groups) {
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
   if (gid >= groups) return;
-  const int ng = (p.N + 3) / 4;
-  const long long row = gid / ng;            // bh * N + i
+  const int ng = (p.Nk + 3) / 4;
+  const long long row = gid / ng;            // bh * Nq + i
   const int jg = (int)(gid - row * ng);
-  const int bh = (int)(row / p.N), i = (int)(row - (long long)bh * p.N);
+  const int bh = (int)(row / p.Nq), i = (int)(row - (long long)bh * p.Nq);
   DropoutStream ds;
   ds.seed_lo = p.seed_lo;
   ds.seed_hi = p.seed_hi;
@@ -450,14 +452,14 @@ __global__ __launch_bounds__(256) void dropout_keep_mask_kernel(FwdParams p, uin
   ds.offset = p.drop_offset;
   ds.thresh = p.drop_thresh;
   const uint32_t bits = ds.keep4((uint32_t)jg, (uint32_t)i);
-  uint8_t* out = keep + row * p.N + 4 * jg;
+  uint8_t* out = keep + row * p.Nk + 4 * jg;
 #pragma unroll
   for (int t = 0; t < 4; ++t)
-    if (4 * jg + t < p.N) out[t] = (uint8_t)((bits >> t) & 1u);
+    if (4 * jg + t < p.Nk) out[t] = (uint8_t)((bits >> t) & 1u);
 }
 
 hipError_t launch_dropout_keep_mask(const FwdParams& p, uint8_t* keep, hipStream_t stream) {
-  const long long groups = (long long)p.BH * p.N * ((p.N + 3) / 4);
+  const long long groups = (long long)p.BH * p.Nq * ((p.Nk + 3) / 4);
   const long long blocks = (groups + 255) / 256;
   hipLaunchKernelGGL(dropout_keep_mask_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p,
                      keep, groups);

@@ -15,10 +15,10 @@ struct FwdParams {
   float* LSE;
   const uint8_t* blockmask;  // nullptr unless block-sparse
   int BH;                    // batch * heads
-  int N;                     // sequence length
-  int nqb;                   // ceil(N / 128) query blocks
+  int Nq, Nk;                // query rows, key rows (equal for self attention)
+  int nqb;                   // ceil(Nq / 128) query blocks
   int mask_block;            // block-mask granularity (multiple of 128)
-  int nbm;                   // ceil(N / mask_block)
+  int nbm;                   // ceil(Nk / mask_block): row stride of the block mask
   float scale_log2;          // scale * log2(e)
   // dropout on P (read only by the dropout kernels): element (i, j) of head bh
   // is kept iff philox4x32_10(j/4, i, bh, drop_offset; seed)[j % 4] >= drop_thresh
@@ -40,11 +40,11 @@ struct BwdParams {
   uint16_t* dV;
   const uint8_t* blockmask;
   int BH;
-  int N;
-  int nqb;                   // ceil(N / 128)
-  int nkb;                   // ceil(N / 128) key blocks for the dK/dV kernel
+  int Nq, Nk;                // query rows, key rows
+  int nqb;                   // ceil(Nq / 128) query blocks for the dQ kernel
+  int nkb;                   // ceil(Nk / 128) key blocks for the dK/dV kernel
   int mask_block;
-  int nbm;
+  int nbm;                   // ceil(Nk / mask_block): row stride of the block mask
   float scale;               // softmax scale
   float scale_log2;          // scale * log2(e)
   // dropout on P (read only by the dropout kernels): element (i, j) of head bh
@@ -57,7 +57,7 @@ struct BwdParams {
 // dropout: the DROPOUT instantiation (p.drop_* and p.seed_* must be set)
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool sparse, bool dropout,
                       hipStream_t stream);
-// keep[bh][i][j] (uint8) of the dropout stream set in p (BH, N, drop_*, seed_*)
+// keep[bh][i][j] (uint8) of the dropout stream set in p (BH, Nq, Nk, drop_*, seed_*)
 hipError_t launch_dropout_keep_mask(const FwdParams& p, uint8_t* keep, hipStream_t stream);
 hipError_t launch_bwd_dsum(const BwdParams& p, int d, hipStream_t stream);
 hipError_t launch_bwd_dkdv(const BwdParams& p, int d, bool causal, bool sparse, bool dropout,

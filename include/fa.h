@@ -169,6 +169,34 @@ int fa_bwd_dq_dsum(const void* Q, const void* K, const void* V, const void* O,
                    float* Dsum, void* dQ, hipStream_t stream);
 
 /*
+ * Attention with N_q query rows and N_k key rows (cross attention, and the
+ * decoding case with a KV cache, which the pages leave untreated:
+ * FlashAttention-NeurIPS22 digest, "设计取舍" (boundary conditions) and
+ * "Critical Analysis" (假设压力测试) note that the decode phase with a growing
+ * KV cache is not characterised).  Q, O, dO, dQ are
+ * [B, H, Nq, d], K, V, dK, dV are [B, H, Nk, d], LSE [B, H, Nq]; a block mask
+ * is ceil(Nq / mask_block) x ceil(Nk / mask_block).  The causal mask is
+ * aligned bottom-right: query i sees key j iff j <= i + (Nk - Nq), i.e. the
+ * queries are the last Nq positions of the key sequence; rows with
+ * i + Nk - Nq < 0 see no key (O = 0, LSE = -inf, dQ = 0).  With Nq = Nk these
+ * are exactly fa_fwd and fa_bwd.  Nk = 0 is allowed (every row empty; K, V,
+ * dK, dV may then be NULL); with Nq = 0 and Nk > 0 fa_bwd_nqk writes dK = dV
+ * = 0.  The workspace is fa_bwd_workspace_bytes(B, H, Nq, d).  Errors as for
+ * fa_fwd and fa_bwd.
+ */
+int fa_fwd_nqk(const void* Q, const void* K, const void* V,
+               int B, int H, int Nq, int Nk, int d, float scale, int causal,
+               const uint8_t* blockmask, int mask_block,
+               void* O, float* LSE, hipStream_t stream);
+
+int fa_bwd_nqk(const void* Q, const void* K, const void* V, const void* O,
+               const void* dO, const float* LSE,
+               int B, int H, int Nq, int Nk, int d, float scale, int causal,
+               const uint8_t* blockmask, int mask_block,
+               void* dQ, void* dK, void* dV,
+               void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
  * Dropout on the attention probabilities.  The pages list dropout among the
  * steps fused into the single attention kernel, between the softmax and the
  * second product (FlashAttention-NeurIPS22 digest, "核心方法", Kernel

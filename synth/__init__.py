@@ -34,6 +34,7 @@ __all__ = [
     "butterfly_blockmask",
     "make_blockmask",
     "draw_inputs",
+    "draw_inputs_nqk",
 ]
 
 
@@ -164,3 +165,14 @@ def draw_inputs(B: int, H: int, N: int, d: int, seed: int, qk_mult: float = 1.0,
 
 def config_inputs(cfg: Config) -> dict[str, np.ndarray]:
     return draw_inputs(cfg.B, cfg.H, cfg.N, cfg.d, cfg.seed, cfg.qk_mult, with_do=True)
+
+
+def draw_inputs_nqk(B: int, H: int, Nq: int, Nk: int, d: int, seed: int) -> dict[str, np.ndarray]:
+    """Seeded Q, dO of shape (B, H, Nq, d) and K, V of shape (B, H, Nk, d), as uint16
+    bf16 bit arrays, drawn in the order Q, K, V, dO from N(0, 1)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {}
+    for name, n in (("q", Nq), ("k", Nk), ("v", Nk), ("do", Nq)):
+        out[name] = bf16_round_bits(rng.standard_normal((B, H, n, d), dtype=np.float32))
+    return out
+

@@ -25,7 +25,8 @@ def test_exports_every_declared_symbol(lib):
     names = fa.header_functions()
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_strerror",
                           "fa_bwd_dsum", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dq_dsum",
-                          "fa_fwd_dropout", "fa_bwd_dropout", "fa_dropout_keep_mask"}
+                          "fa_fwd_dropout", "fa_bwd_dropout", "fa_dropout_keep_mask",
+                          "fa_fwd_nqk", "fa_bwd_nqk"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -182,3 +183,32 @@ def test_dropout_entry_points_validate(lib):
     assert lib.fa_dropout_keep_mask(1, 1, 0, 0.5, 0, 0, None, None) == fa.FA_OK
     assert lib.fa_dropout_keep_mask(64, 64, 1 << 17, 0.5, 0, 0, FAKE, None) == \
         fa.FA_ERR_UNSUPPORTED
+
+
+def fwdq(lib, Nq=128, Nk=64, d=64, q=FAKE, k=FAKE, o=FAKE, bm=None, mb=0, scale=0.125):
+    return lib.fa_fwd_nqk(q, k, k, 1, 1, Nq, Nk, d, scale, 1, bm, mb, o, FAKE, None)
+
+
+def bwdq(lib, Nq=128, Nk=64, q=FAKE, k=FAKE, dk=FAKE, ws=FAKE):
+    return lib.fa_bwd_nqk(q, k, k, FAKE, FAKE, FAKE, 1, 1, Nq, Nk, 64, 0.125, 1, None, 0,
+                          FAKE, dk, dk, ws, 1 << 20, None)
+
+
+def test_nqk_entry_points_validate(lib):
+    for call in (fwdq, bwdq):
+        assert call(lib, Nq=-1) == fa.FA_ERR_SHAPE
+        assert call(lib, Nk=-1) == fa.FA_ERR_SHAPE
+        assert call(lib, Nq=0, Nk=0) == fa.FA_OK
+        assert call(lib, q=None) == fa.FA_ERR_NULL
+    assert fwdq(lib, d=80) == fa.FA_ERR_UNSUPPORTED
+    assert fwdq(lib, scale=0.0) == fa.FA_ERR_UNSUPPORTED
+    assert fwdq(lib, bm=FAKE, mb=64) == fa.FA_ERR_UNSUPPORTED
+    assert fwdq(lib, o=None) == fa.FA_ERR_NULL
+    assert fwdq(lib, k=None) == fa.FA_ERR_NULL           # keys present but K missing
+    assert fwdq(lib, k=FAKE + 4) == fa.FA_ERR_UNSUPPORTED
+    assert fwdq(lib, Nq=0, q=None, o=None) == fa.FA_OK   # no query rows: nothing to do
+    assert bwdq(lib, dk=None) == fa.FA_ERR_NULL
+    assert bwdq(lib, ws=None) == fa.FA_ERR_WORKSPACE
+    # no query rows but keys: dK = dV = 0 must still be written, so dK is required
+    assert bwdq(lib, Nq=0, q=None, dk=None) == fa.FA_ERR_NULL
+    assert fwdq(lib, Nq=1 << 24, Nk=1 << 24, d=128) == fa.FA_ERR_UNSUPPORTED
