@@ -128,6 +128,53 @@ def cpu_baseline(cfg, bits, budget_s: float, gpu_out=None):
     return cpu, worst
 
 
+def decode_bench(args, torch, fa, dev):
+    """One decoding step (B=8, H=16, Nq=1, Nk=args.decode, d=128, causal): the split-KV
+    forward against the unsplit one.  Decoding is bound by reading K and V once, so the
+    figure is K+V bytes per second against the 8 TB/s HBM peak."""
+    B, H, Nq, Nk, d = 8, 16, 1, args.decode, 128
+    bits = synth.draw_inputs_nqk(B, H, Nq, Nk, d, 4242)
+
+    def up(x):
+        return torch.from_numpy(x.view(np.int16)).to(dev).view(torch.bfloat16)
+
+    q, k, v = (up(bits[x]) for x in ("q", "k", "v"))
+    scale = d ** -0.5
+    splits = fa.splitkv_num_splits(B, H, Nq, Nk, d)
+    o, lse = torch.empty_like(q), torch.empty((B, H, Nq), dtype=torch.float32, device=dev)
+    timings = {}
+    for name, fn in (("splitkv", lambda: fa.forward_splitkv(q, k, v, scale, True, out=o, lse=lse)),
+                     ("unsplit", lambda: fa.forward(q, k, v, scale, True, out=o, lse=lse))):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        timings[name] = e0.elapsed_time(e1) / args.steps
+    kv_bytes = 2.0 * B * H * Nk * d * 2
+    gbs = {n: kv_bytes / (t * 1e-3) / 1e9 for n, t in timings.items()}
+    log(f"[bench] decode B{B} H{H} Nq{Nq} Nk{Nk} d{d}: split-KV ({splits} splits) "
+        f"{timings['splitkv'] * 1e3:.1f} us = {gbs['splitkv']:.0f} GB/s; unsplit "
+        f"{timings['unsplit'] * 1e3:.1f} us = {gbs['unsplit']:.0f} GB/s")
+    line = {
+        "metric": "decode attention: K+V bytes read per second (one query row per head)",
+        "value": gbs["splitkv"], "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": timings["splitkv"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"decode: B={B} H={H} Nq={Nq} Nk={Nk} d={d} causal, split-KV",
+                   "splits": splits, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": gbs["splitkv"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": gbs["splitkv"] / PEAK_HBM_GBS, "traffic": None},
+        "unsplit_GBps": gbs["unsplit"],
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,6 +184,10 @@ def main():
     ap.add_argument("--dropout", type=float, default=0.0,
                     help="dropout probability on P (0 = none, the default workload); with "
                          "p > 0 the step is fa_fwd_dropout + fa_bwd_dropout, timed as two parts")
+    ap.add_argument("--decode", type=int, default=0, metavar="NK",
+                    help="instead of the training step, time one decoding step: B=8 H=16, one "
+                         "query row per head against an NK-key cache (d=128, causal), "
+                         "split-KV forward and the unsplit forward, as HBM GB/s of K and V")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the oracle timed on host cores (0 disables it)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -166,6 +217,8 @@ def main():
         sys.exit(1)
     fa.load_library()
     dev = torch.device("cuda:0")
+    if args.decode > 0:
+        return decode_bench(args, torch, fa, dev)
     cfg = synth.CONFIGS[args.workload]
     B, H, N, d = cfg.shape()
     bits = synth.config_inputs(cfg)

@@ -54,6 +54,10 @@ _SIGNATURES = {
     "fa_fwd_nqk": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _i, _vp, _vp, _vp]),
     "fa_bwd_nqk": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _i,
                         _vp, _vp, _vp, _vp, _sz, _vp]),
+    "fa_fwd_splitkv": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _i, _f, _i, _vp, _i, _i, _vp, _sz,
+                            _vp, _vp, _vp]),
+    "fa_fwd_splitkv_num_splits": (_i, [_i, _i, _i, _i, _i]),
+    "fa_fwd_splitkv_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
     "fa_strerror": (ctypes.c_char_p, [_i]),
 }
 
@@ -388,3 +392,39 @@ class FlashAttention:
 
             cls._fn = _Fn
         return cls._fn.apply(q, k, v, scale, causal, blockmask, mask_block)
+
+
+def splitkv_num_splits(B: int, H: int, Nq: int, Nk: int, d: int) -> int:
+    """The split count fa_fwd_splitkv chooses by itself."""
+    return int(load_library().fa_fwd_splitkv_num_splits(B, H, Nq, Nk, d))
+
+
+def forward_splitkv(q, k, v, scale: float | None = None, causal: bool = False, blockmask=None,
+                    mask_block: int = 128, num_splits: int = 0, out=None, lse=None):
+    """Forward with the key axis split across workgroups (decoding shapes: few
+    query rows, long K/V).  Same results as ``forward`` up to rounding."""
+    torch = _torch()
+    _check(q, "q", torch.bfloat16)
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
+    B, H, N, d = q.shape
+    Nk = k.shape[2]
+    dev = q.device
+    _check(k, "k", torch.bfloat16, (B, H, Nk, d), dev)
+    _check(v, "v", torch.bfloat16, (B, H, Nk, d), dev)
+    scale = default_scale(d) if scale is None else float(scale)
+    out = torch.empty_like(q) if out is None else out
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev) if lse is None else lse
+    _check(out, "out", torch.bfloat16, q.shape, dev)
+    _check(lse, "lse", torch.float32, (B, H, N), dev)
+    lib = load_library()
+    nbytes = int(lib.fa_fwd_splitkv_workspace_bytes(B, H, N, Nk, d, int(num_splits)))
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    bm_ptr, mb = _mask_args(blockmask, N, mask_block, dev, Nk)
+    rc = lib.fa_fwd_splitkv(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, Nk, d, scale,
+                            int(bool(causal)), bm_ptr, mb, int(num_splits), ws.data_ptr(),
+                            ws.numel(), out.data_ptr(), lse.data_ptr(), _stream_ptr(dev))
+    if rc != FA_OK:
+        raise LibfaError(rc, "fa_fwd_splitkv")
+    return out, lse
+

@@ -6,6 +6,7 @@
 
 #include "fa.h"
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <initializer_list>
@@ -119,9 +120,35 @@ void set_dropout(Params& p, float p_drop, uint64_t seed, uint32_t offset) {
   p.drop_offset = offset;
 }
 
+// Split-KV layout: how many key ranges per query block (1 = no split).  Asked
+// for <= 0, the count aims at 2048 workgroups in flight (8 per CU), with at
+// least four 64-key tiles per range; the count is then trimmed so that no
+// range is empty.
+int splitkv_splits(int B, int H, int Nq, int Nk, int requested, int* tiles_per_split) {
+  const long long nqb = ((long long)Nq + 127) / 128;
+  const long long tiles = ((long long)Nk + 63) / 64;
+  const long long wg = nqb * B * H;
+  long long s = requested;
+  if (s <= 0) {
+    s = wg > 0 ? (2048 + wg - 1) / wg : 1;
+    s = std::min(s, (tiles + 3) / 4);
+  }
+  s = std::max(1LL, std::min(s, std::max(1LL, tiles)));
+  const long long tps = (tiles + s - 1) / s;
+  s = tps > 0 ? (tiles + tps - 1) / tps : 1;
+  *tiles_per_split = (int)std::max(1LL, tps);
+  return (int)std::max(1LL, s);
+}
+
+size_t splitkv_bytes(int B, int H, int Nq, int d, int splits) {
+  if (splits <= 1) return 0;
+  return (size_t)splits * B * H * Nq * (size_t)(d + 1) * 4;
+}
+
 int fwd_impl(const void* Q, const void* K, const void* V, int B, int H, int Nq, int Nk, int d,
              float scale, int causal, const uint8_t* blockmask, int mask_block, float p_drop,
-             uint64_t seed, uint32_t offset, void* O, float* LSE, hipStream_t stream) {
+             uint64_t seed, uint32_t offset, void* O, float* LSE, hipStream_t stream,
+             int num_splits = 1, void* workspace = nullptr, size_t workspace_bytes = 0) {
   bool empty = false;
   int rc = check_common(B, H, Nq, Nk, d, scale, blockmask, mask_block, &empty);
   if (rc != FA_OK) return rc;
@@ -147,6 +174,19 @@ int fwd_impl(const void* Q, const void* K, const void* V, int B, int H, int Nq, 
   p.nbm = (Nk + p.mask_block - 1) / p.mask_block;
   p.scale_log2 = scale * kLog2e;
   set_dropout(p, p_drop, seed, offset);
+  p.nsplit = 1;
+  p.tiles_per_split = 0;
+  p.Opart = p.LSEpart = nullptr;
+  if (num_splits != 1 && p_drop == 0.f) {
+    p.nsplit = splitkv_splits(B, H, Nq, Nk, num_splits, &p.tiles_per_split);
+    if (p.nsplit > 1) {
+      const size_t need = splitkv_bytes(B, H, Nq, d, p.nsplit);
+      if (!workspace || workspace_bytes < need) return FA_ERR_WORKSPACE;
+      if (!aligned(workspace, 16)) return FA_ERR_UNSUPPORTED;
+      p.Opart = static_cast<float*>(workspace);
+      p.LSEpart = p.Opart + (size_t)p.nsplit * B * H * Nq * d;
+    }
+  }
   return status_of(
       fa::launch_fwd(p, d, causal != 0, blockmask != nullptr, p_drop > 0.f, stream));
 }
@@ -187,6 +227,28 @@ int fa_fwd_nqk(const void* Q, const void* K, const void* V, int B, int H, int Nq
                float* LSE, hipStream_t stream) {
   return fwd_impl(Q, K, V, B, H, Nq, Nk, d, scale, causal, blockmask, mask_block, 0.f, 0, 0, O,
                   LSE, stream);
+}
+
+int fa_fwd_splitkv_num_splits(int B, int H, int Nq, int Nk, int d) {
+  bool empty = false;
+  if (check_shape(B, H, Nq, Nk, d, &empty) != FA_OK) return 0;
+  int tps = 0;
+  return splitkv_splits(B, H, Nq, Nk, 0, &tps);
+}
+
+size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits) {
+  bool empty = false;
+  if (check_shape(B, H, Nq, Nk, d, &empty) != FA_OK) return 0;
+  int tps = 0;
+  return splitkv_bytes(B, H, Nq, d, splitkv_splits(B, H, Nq, Nk, num_splits, &tps));
+}
+
+int fa_fwd_splitkv(const void* Q, const void* K, const void* V, int B, int H, int Nq, int Nk,
+                   int d, float scale, int causal, const uint8_t* blockmask, int mask_block,
+                   int num_splits, void* workspace, size_t workspace_bytes, void* O, float* LSE,
+                   hipStream_t stream) {
+  return fwd_impl(Q, K, V, B, H, Nq, Nk, d, scale, causal, blockmask, mask_block, 0.f, 0, 0, O,
+                  LSE, stream, num_splits <= 0 ? 0 : num_splits, workspace, workspace_bytes);
 }
 
 int fa_fwd_dropout(const void* Q, const void* K, const void* V, int B, int H, int N, int d,

@@ -47,8 +47,13 @@ namespace fa {
 // sum, and with it LSE, stays that of the plain softmax).  The keep bits of a
 // tile come from the head's Philox stream (DropoutStream) and are drawn while
 // the tile's scores are on the matrix cores.
-template <int D, bool CAUSAL, bool SPARSE, bool DROPOUT>
+// MODE 2 (split-KV): the key tiles of a query block are split into p.nsplit
+// ranges of p.tiles_per_split tiles, one workgroup each; a workgroup writes
+// its normalised partial O (fp32) and partial LSE to p.Opart / p.LSEpart, and
+// combine_kernel merges the ranges with the log-sum-exp rule.
+template <int D, bool CAUSAL, bool SPARSE, int MODE>
 __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
+  constexpr bool DROPOUT = MODE == 1, SPLIT = MODE == 2;
   constexpr int BQ = 128, BK = 64, NW = 4;
   constexpr float kSlack = 8.0f;
   constexpr int NDB = D / 32;   // 32-wide column blocks of O^T
@@ -68,9 +73,11 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const BlockCoord bc = block_coord(p.nqb);
+  const BlockCoord bc = block_coord(SPLIT ? p.nqb * p.nsplit : p.nqb);
+  const int qblk = SPLIT ? bc.blk / p.nsplit : bc.blk;
+  const int split = SPLIT ? bc.blk - qblk * p.nsplit : 0;
   // heaviest query blocks first under the causal mask
-  const int qb = CAUSAL ? (p.nqb - 1 - bc.blk) : bc.blk;
+  const int qb = CAUSAL ? (p.nqb - 1 - qblk) : qblk;
   // Nq queries, Nk keys; under the causal mask query i sees key j iff
   // j <= i + dlt (the queries are the last Nq positions of the key sequence)
   const int Nq = p.Nq, Nk = p.Nk, dlt = Nk - Nq;
@@ -91,7 +98,10 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 
   // key range and tile schedule
   const int kend = CAUSAL ? max(0, min(Nk, (qb + 1) * BQ + dlt)) : Nk;
-  const int ntiles = (kend + BK - 1) / BK;
+  // tiles [tbeg, ntiles): all of the visible range, or this workgroup's split of it
+  const int tbeg = SPLIT ? split * p.tiles_per_split : 0;
+  const int ntiles = SPLIT ? min((kend + BK - 1) / BK, tbeg + p.tiles_per_split)
+                           : (kend + BK - 1) / BK;
   const int mrow = SPARSE ? (qb * BQ) / p.mask_block : 0;
   auto next_tile = [&](int t) FA_INLINE -> int {
     if constexpr (SPARSE) {
@@ -342,6 +352,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   // One iteration for tile tc, whose K is in K buffer PAR; the previous
   // tile's V is in V buffer 1 - PAR and its probabilities in pb.  FIRST:
   // there is no previous tile (O is still zero).
+  const bool wave_has_rows = q0w < Nq;
   auto iteration = [&](auto parc, auto firstc, int& tc, int& tn) FA_INLINE {
     constexpr int PAR = decltype(parc)::value;
     constexpr bool FIRST = decltype(firstc)::value;
@@ -353,18 +364,22 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     // A tile entirely above this wavefront's causal diagonal is processed
     // like any other: the mask sets all its scores to -inf, so its P is 0
     // and O is unchanged.  One code path keeps O in one register set.
-    phaseA(PAR ? kbuf1 : kbuf0, tc);
-    mask(tc);
-    if constexpr (FIRST) {
-      rowmax_part1();
-      rowmax_part2();
-      exponentiate(sc, pb);
-      l_run += rowsum(sc);
-    } else {
-      float alpha;
-      const float psum = phaseB(PAR ? vbuf0 : vbuf1, alpha);   // scales l_run by alpha
-      l_run += psum;
-      rescale(alpha);
+    // (Split-KV serves decoding, where a query block has few rows: a
+    // wavefront with none only helps copy the tiles.)
+    if (!SPLIT || wave_has_rows) {
+      phaseA(PAR ? kbuf1 : kbuf0, tc);
+      mask(tc);
+      if constexpr (FIRST) {
+        rowmax_part1();
+        rowmax_part2();
+        exponentiate(sc, pb);
+        l_run += rowsum(sc);
+      } else {
+        float alpha;
+        const float psum = phaseB(PAR ? vbuf0 : vbuf1, alpha);   // scales l_run by alpha
+        l_run += psum;
+        rescale(alpha);
+      }
     }
     tc = tn;
     tn = tn2;
@@ -372,7 +387,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 
   using P0 = std::integral_constant<int, 0>;
   using P1 = std::integral_constant<int, 1>;
-  int tc = next_tile(0);
+  int tc = next_tile(tbeg);
   int tn = tc < ntiles ? next_tile(tc + 1) : ntiles;
   if (tc < ntiles) {
     load_k(tc, 0);
@@ -388,13 +403,33 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     // the last tile's P V product
     wait_vmem();
     __syncthreads();
-    if (odd) pv_only(vbuf1);
-    else pv_only(vbuf0);
+    if (!SPLIT || wave_has_rows) {
+      if (odd) pv_only(vbuf1);
+      else pv_only(vbuf0);
+    }
   }
 
   // epilogue: combine the two lane halves' partial sums, divide once
   const float l_tot = sum_xor32(l_run);
   const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  if constexpr (SPLIT) {
+    if (qrow < Nq) {
+      const size_t prow = ((size_t)split * p.BH + bc.bh) * Nq + qrow;
+      float* Op = p.Opart + prow * D;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          f32x4 v;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = oacc[db][qd * 4 + e] * inv;
+          *reinterpret_cast<f32x4*>(Op + db * 32 + qd * 8 + g * 4) = v;
+        }
+      if (g == 0)
+        p.LSEpart[prow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    }
+    return;
+  }
   if (qrow < Nq) {
     uint16_t* Oh = p.O + qhead + (size_t)qrow * D;
 #pragma unroll
@@ -411,28 +446,67 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   }
 }
 
+// Merge of the split-KV partial results of one row: LSE = log sum_s exp(LSE_s)
+// and O = sum_s exp(LSE_s - LSE) O_s (each O_s is normalised by its own row
+// sum), O rounded to bf16.  A row with no visible key in any split gets
+// O = 0, LSE = -inf.  Thread = four columns of one row.
+template <int D>
+__global__ __launch_bounds__(256) void combine_kernel(FwdParams p, long long rows) {
+  constexpr int TPR = D / 4, RPB = 256 / TPR;
+  const long long row = (long long)blockIdx.x * RPB + threadIdx.x / TPR;
+  const int col = (threadIdx.x % TPR) * 4;
+  if (row >= rows) return;
+  const int ns = p.nsplit;
+  float m = -INFINITY;
+  for (int sidx = 0; sidx < ns; ++sidx) m = fmaxf(m, p.LSEpart[(size_t)sidx * rows + row]);
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  float wsum = 0.f;
+  if (m != -INFINITY) {
+    for (int sidx = 0; sidx < ns; ++sidx) {
+      const float w = __expf(p.LSEpart[(size_t)sidx * rows + row] - m);
+      wsum += w;
+      const f32x4 o = *reinterpret_cast<const f32x4*>(p.Opart + ((size_t)sidx * rows + row) * D + col);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, o[e], acc[e]);
+    }
+  }
+  const float inv = wsum > 0.f ? 1.f / wsum : 0.f;
+  *reinterpret_cast<u32x2*>(p.O + row * D + col) =
+      pack_bf16x4(acc[0] * inv, acc[1] * inv, acc[2] * inv, acc[3] * inv);
+  if (col == 0) p.LSE[row] = wsum > 0.f ? m + __logf(wsum) : -INFINITY;
+}
+
 template <int D, bool CAUSAL, bool SPARSE>
-static hipError_t launch_fwd_t(const FwdParams& p, bool dropout, hipStream_t stream) {
-  const dim3 grid((unsigned)((long long)p.nqb * p.BH));
-  if (dropout)
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, SPARSE, true>), grid, dim3(256), 0, stream, p);
+static hipError_t launch_fwd_t(const FwdParams& p, int mode, hipStream_t stream) {
+  const dim3 grid((unsigned)((long long)p.nqb * p.BH * (mode == 2 ? p.nsplit : 1)));
+  if (mode == 1)
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, SPARSE, 1>), grid, dim3(256), 0, stream, p);
+  else if (mode == 2)
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, SPARSE, 2>), grid, dim3(256), 0, stream, p);
   else
-    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, SPARSE, false>), grid, dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((fwd_kernel<D, CAUSAL, SPARSE, 0>), grid, dim3(256), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || mode != 2) return e;
+  const long long rows = (long long)p.BH * p.Nq;
+  constexpr int RPB = 256 / (D / 4);
+  hipLaunchKernelGGL((combine_kernel<D>), dim3((unsigned)((rows + RPB - 1) / RPB)), dim3(256), 0,
+                     stream, p, rows);
   return hipGetLastError();
 }
 
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool sparse, bool dropout,
                       hipStream_t stream) {
+  const int mode = dropout ? 1 : (p.nsplit > 1 ? 2 : 0);
   if (d == 64) {
-    if (causal) return sparse ? launch_fwd_t<64, true, true>(p, dropout, stream)
-                              : launch_fwd_t<64, true, false>(p, dropout, stream);
-    return sparse ? launch_fwd_t<64, false, true>(p, dropout, stream)
-                  : launch_fwd_t<64, false, false>(p, dropout, stream);
+    if (causal) return sparse ? launch_fwd_t<64, true, true>(p, mode, stream)
+                              : launch_fwd_t<64, true, false>(p, mode, stream);
+    return sparse ? launch_fwd_t<64, false, true>(p, mode, stream)
+                  : launch_fwd_t<64, false, false>(p, mode, stream);
   }
-  if (causal) return sparse ? launch_fwd_t<128, true, true>(p, dropout, stream)
-                            : launch_fwd_t<128, true, false>(p, dropout, stream);
-  return sparse ? launch_fwd_t<128, false, true>(p, dropout, stream)
-                : launch_fwd_t<128, false, false>(p, dropout, stream);
+  if (causal) return sparse ? launch_fwd_t<128, true, true>(p, mode, stream)
+                            : launch_fwd_t<128, true, false>(p, mode, stream);
+  return sparse ? launch_fwd_t<128, false, true>(p, mode, stream)
+                : launch_fwd_t<128, false, false>(p, mode, stream);
 }
 
 // Keep mask of the dropout stream, keep[bh][i][j] = 1 or 0, for inspection and

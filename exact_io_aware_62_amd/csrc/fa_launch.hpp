@@ -20,6 +20,10 @@ struct FwdParams {
   int mask_block;            // block-mask granularity (multiple of 128)
   int nbm;                   // ceil(Nk / mask_block): row stride of the block mask
   float scale_log2;          // scale * log2(e)
+  // split-KV (nsplit > 1): partial results [nsplit][BH][Nq][D] and [nsplit][BH][Nq]
+  int nsplit, tiles_per_split;
+  float* Opart;
+  float* LSEpart;
   // dropout on P (read only by the dropout kernels): element (i, j) of head bh
   // is kept iff philox4x32_10(j/4, i, bh, drop_offset; seed)[j % 4] >= drop_thresh
   uint32_t drop_thresh;      // floor(p * 2^32)
@@ -54,7 +58,8 @@ struct BwdParams {
   uint32_t seed_lo, seed_hi, drop_offset;
 };
 
-// dropout: the DROPOUT instantiation (p.drop_* and p.seed_* must be set)
+// dropout: the DROPOUT instantiation (p.drop_* and p.seed_* must be set);
+// otherwise p.nsplit > 1 selects split-KV (p.Opart / p.LSEpart) plus the merge
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool sparse, bool dropout,
                       hipStream_t stream);
 // keep[bh][i][j] (uint8) of the dropout stream set in p (BH, Nq, Nk, drop_*, seed_*)

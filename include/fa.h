@@ -197,6 +197,40 @@ int fa_bwd_nqk(const void* Q, const void* K, const void* V, const void* O,
                void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Forward with the key axis split across workgroups (split-KV), for shapes with
+ * few query rows and a long key sequence (decoding against a KV cache), where
+ * one workgroup per 128 query rows and head would leave most of the GPU idle.
+ * The key tiles of each query block are cut into num_splits ranges; each range
+ * produces a normalised partial O_s and its LSE_s in the workspace, and a
+ * second launch merges them: LSE = log sum_s exp(LSE_s), O = sum_s
+ * exp(LSE_s - LSE) O_s, which is the softmax over all keys (the same
+ * rescaling identity the online softmax applies tile by tile, digest "核心方法",
+ * Tiling 与 online softmax).  Arguments and results are those of fa_fwd_nqk.
+ *   num_splits  <= 0: chosen by fa_fwd_splitkv_num_splits; 1: no split (then
+ *               exactly fa_fwd_nqk, workspace unused).  Counts beyond the
+ *               number of 64-key tiles are reduced.
+ *   workspace   DEVICE, 16-byte aligned, at least
+ *               fa_fwd_splitkv_workspace_bytes(B, H, Nq, Nk, d, num_splits)
+ *               bytes (0 when no split results); else FA_ERR_WORKSPACE.
+ * Results agree with fa_fwd_nqk to rounding (the merge adds up to num_splits
+ * fp32 terms per element); not bitwise.
+ */
+int fa_fwd_splitkv(const void* Q, const void* K, const void* V,
+                   int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                   const uint8_t* blockmask, int mask_block, int num_splits,
+                   void* workspace, size_t workspace_bytes,
+                   void* O, float* LSE, hipStream_t stream);
+
+/* The split count fa_fwd_splitkv uses for num_splits <= 0 (at least 1): about
+ * 2048 workgroups in flight with at least four 64-key tiles per range; 0 for
+ * invalid shapes. */
+int fa_fwd_splitkv_num_splits(int B, int H, int Nq, int Nk, int d);
+
+/* Workspace bytes fa_fwd_splitkv needs for that num_splits (0: no split, or
+ * invalid shapes): splits * B * H * Nq * (d + 1) * 4. */
+size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int num_splits);
+
+/*
  * Dropout on the attention probabilities.  The pages list dropout among the
  * steps fused into the single attention kernel, between the softmax and the
  * second product (FlashAttention-NeurIPS22 digest, "核心方法", Kernel

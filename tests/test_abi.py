@@ -26,7 +26,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"fa_fwd", "fa_bwd", "fa_bwd_workspace_bytes", "fa_strerror",
                           "fa_bwd_dsum", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dq_dsum",
                           "fa_fwd_dropout", "fa_bwd_dropout", "fa_dropout_keep_mask",
-                          "fa_fwd_nqk", "fa_bwd_nqk"}
+                          "fa_fwd_nqk", "fa_bwd_nqk", "fa_fwd_splitkv",
+                          "fa_fwd_splitkv_num_splits", "fa_fwd_splitkv_workspace_bytes"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -212,3 +213,31 @@ def test_nqk_entry_points_validate(lib):
     # no query rows but keys: dK = dV = 0 must still be written, so dK is required
     assert bwdq(lib, Nq=0, q=None, dk=None) == fa.FA_ERR_NULL
     assert fwdq(lib, Nq=1 << 24, Nk=1 << 24, d=128) == fa.FA_ERR_UNSUPPORTED
+
+
+def test_splitkv_sizing_and_validation(lib):
+    # decoding: one query row per head, long cache -> many splits, >= 4 tiles each
+    s = lib.fa_fwd_splitkv_num_splits(8, 16, 1, 16384, 128)
+    assert s == 16      # 2048 workgroups / 128 heads, 256 tiles -> 16 tiles per range
+    assert lib.fa_fwd_splitkv_workspace_bytes(8, 16, 1, 16384, 128, 0) == 16 * 128 * 129 * 4
+    # short caches: at least four tiles per range
+    assert lib.fa_fwd_splitkv_num_splits(1, 1, 1, 512, 64) == 2
+    # a full training shape needs no split
+    assert lib.fa_fwd_splitkv_num_splits(8, 16, 2048, 2048, 128) == 1
+    assert lib.fa_fwd_splitkv_workspace_bytes(8, 16, 2048, 2048, 128, 0) == 0
+    # explicit counts: trimmed to the tile count, empty ranges removed
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, 1, 1, 640, 64, 1000) == 10 * 65 * 4
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, 1, 1, 640, 64, 4) == 4 * 65 * 4
+    assert lib.fa_fwd_splitkv_workspace_bytes(1, 1, 1, 640, 64, 1) == 0
+    assert lib.fa_fwd_splitkv_num_splits(1, 1, 1, 640, 96) == 0
+    assert lib.fa_fwd_splitkv_workspace_bytes(-1, 1, 1, 640, 64, 4) == 0
+
+    def call(ws=FAKE, wsb=1 << 30, Nq=1, Nk=4096, splits=0, d=128):
+        return lib.fa_fwd_splitkv(FAKE, FAKE, FAKE, 1, 1, Nq, Nk, d, 0.1, 1, None, 0, splits,
+                                  ws, wsb, FAKE, FAKE, None)
+    assert call(ws=None) == fa.FA_ERR_WORKSPACE
+    assert call(wsb=16) == fa.FA_ERR_WORKSPACE
+    assert call(ws=FAKE + 4) == fa.FA_ERR_UNSUPPORTED
+    assert call(d=48) == fa.FA_ERR_UNSUPPORTED
+    assert call(Nq=-1) == fa.FA_ERR_SHAPE
+    assert call(Nq=0) == fa.FA_OK
