@@ -205,21 +205,22 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   // Row max of the tile as a tree of max3 (depth 4 instead of a chain of 16),
   // in two parts so that each part fits under one matrix product.
   float mx4[4];
+  // (Only three-input maxima: a two-input maximum of raw products costs two
+  // extra canonicalising instructions.)
   auto rowmax_part1 = [&]() FA_INLINE {
-    float t[11];
+    float t[10];
 #pragma unroll
     for (int u = 0; u < 10; ++u) {
       const int e = 3 * u;
       t[u] = __builtin_fmaxf(__builtin_fmaxf(sc[e >> 4][e & 15], sc[(e + 1) >> 4][(e + 1) & 15]),
                              sc[(e + 2) >> 4][(e + 2) & 15]);
     }
-    t[10] = __builtin_fmaxf(sc[1][14], sc[1][15]);
 #pragma unroll
     for (int u = 0; u < 3; ++u) {
       mx4[u] = __builtin_fmaxf(__builtin_fmaxf(t[3 * u], t[3 * u + 1]), t[3 * u + 2]);
       pin(mx4[u]);
     }
-    mx4[3] = __builtin_fmaxf(t[9], t[10]);
+    mx4[3] = __builtin_fmaxf(__builtin_fmaxf(t[9], sc[1][14]), sc[1][15]);
     pin(mx4[3]);
   };
   // The running maximum only moves when a score exceeds it by more than
@@ -275,19 +276,30 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       // P entry q is last read by product NDB q + NDB - 1; its exps come later
       // (entry q's exps end by product J0 + (8q + 8) (NJ - J0) / 32 - 1 >= NDB q + NDB - 1)
       constexpr int NE = NJ - J0;
+      // this slot's exponentials first, then their sums and packs: a sum
+      // right after the exponential it reads would need a wait state
+      constexpr int EMAX = (32 + NE - 1) / NE + 1;
+      const int e0 = j < J0 ? 0 : (j - J0) * 32 / NE;
+      const int e1 = j < J0 ? 0 : (j + 1 - J0) * 32 / NE;
+      float pes[EMAX];
 #pragma unroll
-      for (int e = j < J0 ? 0 : (j - J0) * 32 / NE; e < (j < J0 ? 0 : (j + 1 - J0) * 32 / NE); ++e) {
+      for (int e = e0; e < e1; ++e) {
         const int b = e >> 4, i = e & 15;
+        pes[e - e0] = exp2_fast(__builtin_fmaf(sc[b][i], c, -m_run));
+        pin(pes[e - e0]);
+      }
+#pragma unroll
+      for (int e = e0; e < e1; ++e) {
+        const int b = e >> 4, i = e & 15;
+        const float pe = pes[e - e0];
+        sc[b][i] = dropped(pe, e);
         // the row sum is taken over the fp32 probabilities: a sum of the
         // bf16-rounded ones would move LSE by up to 2^-9 on short rows
-        float pe = exp2_fast(__builtin_fmaf(sc[b][i], c, -m_run));
-        pin(pe);
-        sc[b][i] = dropped(pe, e);
         if (e & 1) {
-          a1 += pe;
+          a1 = e == 1 ? pe : a1 + pe;
           pin(a1);
         } else {
-          a0 += pe;
+          a0 = e == 0 ? pe : a0 + pe;
           pin(a0);
         }
         if ((i & 7) == 7) {
