@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256, (DROPOUT && D == 128) ? 1 : 2) void dkdv_kerne
   const int tid = threadIdx.x;
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const BlockCoord bc = block_coord(p.nkb);
+  const BlockCoord bc = block_coord(p.nkb, true);
   const int kb = bc.blk;
   // Nq queries, Nk keys; causal: query i sees key j iff j <= i + dlt
   const int Nq = p.Nq, Nk = p.Nk, dlt = Nk - Nq;
@@ -408,7 +408,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const BlockCoord bc = block_coord(p.nqb);
+  const BlockCoord bc = block_coord(p.nqb, !CAUSAL);
   const int qb = CAUSAL ? (p.nqb - 1 - bc.blk) : bc.blk;
   // Nq queries, Nk keys; causal: query i sees key j iff j <= i + dlt
   const int Nq = p.Nq, Nk = p.Nk, dlt = Nk - Nq;

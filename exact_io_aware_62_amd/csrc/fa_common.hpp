@@ -397,20 +397,36 @@ __device__ __forceinline__ OperandAddr<T> operand_addr(int lane) {
   return o;
 }
 
-// Block index -> (query/key block, batch*head), block-major: the first BH ids
-// take block 0 of every head, the next BH block 1, and so on.  Kernels that
-// reverse the block order under a causal mask thereby launch the longest
-// blocks of every head first, which keeps the end of the grid short.
+// Block index -> (query/key block, batch*head).  Workgroups are dispatched
+// round-robin over the 8 XCDs (each with its own L2), so id mod 8 picks the
+// XCD.  Every head's blocks go to one XCD (bh mod 8 = id mod 8), and within an
+// XCD the heads are taken four at a time: all blocks of four heads, block 0
+// (the longest under the causal order of the kernels) first, before the next
+// four.  Each XCD then has about four heads' K and V (or Q and dO) in flight,
+// which its 4 MB L2 can hold, and still starts the long blocks first.
+// Without `grouped`, or when B*H is not a multiple of 32, the order is plain
+// block-major (the first BH ids take block 0 of every head, the next BH block
+// 1, ...): every head's longest block starts first, which measured better for
+// the causal query-block kernels, whose blocks differ most in length.
 struct BlockCoord {
   int blk;
   int bh;
 };
 
-__device__ __forceinline__ BlockCoord block_coord(int nblk) {
+__device__ __forceinline__ BlockCoord block_coord(int nblk, bool grouped) {
   const int BH = (int)gridDim.x / nblk;
+  const int id = (int)blockIdx.x;
   BlockCoord c;
-  c.blk = (int)blockIdx.x / BH;
-  c.bh = (int)blockIdx.x - c.blk * BH;
+  if (grouped && BH % 32 == 0) {
+    constexpr int kXcd = 8, kGroup = 4;
+    const int x = id % kXcd, l = id / kXcd;           // XCD, position on it
+    const int g = l / (kGroup * nblk), rem = l - g * (kGroup * nblk);
+    c.blk = rem / kGroup;
+    c.bh = (g * kGroup + (rem - c.blk * kGroup)) * kXcd + x;
+  } else {
+    c.blk = id / BH;
+    c.bh = id - c.blk * BH;
+  }
   return c;
 }
 

@@ -73,7 +73,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const BlockCoord bc = block_coord(SPLIT ? p.nqb * p.nsplit : p.nqb);
+  const BlockCoord bc = block_coord(SPLIT ? p.nqb * p.nsplit : p.nqb, !CAUSAL);
   const int qblk = SPLIT ? bc.blk / p.nsplit : bc.blk;
   const int split = SPLIT ? bc.blk - qblk * p.nsplit : 0;
   // heaviest query blocks first under the causal mask
