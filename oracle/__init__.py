@@ -30,3 +30,8 @@ from .dropout import (  # noqa: F401
     forward_dropout,
     backward_dropout,
 )
+from .fp8 import (  # noqa: F401
+    e4m3_value,
+    dequantize,
+    head_forward_fp8,
+)

@@ -35,6 +35,8 @@ __all__ = [
     "make_blockmask",
     "draw_inputs",
     "draw_inputs_nqk",
+    "e4m3_round_codes",
+    "draw_inputs_fp8",
 ]
 
 
@@ -176,3 +178,58 @@ def draw_inputs_nqk(B: int, H: int, Nq: int, Nk: int, d: int, seed: int) -> dict
         out[name] = bf16_round_bits(rng.standard_normal((B, H, n, d), dtype=np.float32))
     return out
 
+
+
+# ---------------------------------------------------------------------------
+# FP8 (E4M3) inputs.  A tensor is drawn from N(0, 1) in float32 like the bf16
+# inputs, given one per-tensor factor ``descale`` = max|x| / 448 (float32, so the
+# largest magnitude lands on the largest finite E4M3 value), and stored as the E4M3
+# codes of x / descale, rounded to nearest with ties to the even code.
+# ---------------------------------------------------------------------------
+
+def _e4m3_table() -> np.ndarray:
+    """Magnitudes of the 127 non-negative finite E4M3 codes 0x00 .. 0x7E, in code
+    order (which is also increasing order): 2^-9 steps below 2^-6, then three
+    mantissa bits per binade up to 448."""
+    vals = []
+    for code in range(127):
+        e, m = code >> 3, code & 7
+        vals.append(math.ldexp(m, -9) if e == 0 else math.ldexp(8 + m, e - 10))
+    return np.array(vals, dtype=np.float64)
+
+
+_E4M3 = _e4m3_table()
+
+
+def e4m3_round_codes(x) -> np.ndarray:
+    """float values -> uint8 E4M3 codes, round to nearest, ties to the even code.
+
+    Magnitudes above 448 are an error (the callers scale into range first)."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.abs(x)
+    if np.any(~np.isfinite(a)) or np.any(a > _E4M3[-1]):
+        raise ValueError("value outside the finite E4M3 range")
+    hi = np.clip(np.searchsorted(_E4M3, a, side="left"), 0, 126)
+    lo = np.maximum(hi - 1, 0)
+    dlo, dhi = a - _E4M3[lo], _E4M3[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.uint8)
+    neg = np.signbit(x) & (code != 0)
+    return np.where(neg, code | 0x80, code).astype(np.uint8)
+
+
+def draw_inputs_fp8(B: int, H: int, N: int, d: int, seed: int,
+                    amax: float = 448.0) -> dict[str, np.ndarray]:
+    """Seeded Q, K, V as E4M3 codes (uint8, shape (B, H, N, d)) plus their float32
+    descales under keys "q_descale", "k_descale", "v_descale".
+
+    Draw order Q, K, V from N(0, 1) float32; descale = float32(max|x| / amax)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = {}
+    for name in ("q", "k", "v"):
+        x = rng.standard_normal((B, H, N, d), dtype=np.float32)
+        ds = np.float32(np.abs(x).max() / amax) if x.size else np.float32(1.0)
+        y = x.astype(np.float64) / float(ds)
+        out[name] = e4m3_round_codes(np.clip(y, -amax, amax))
+        out[name + "_descale"] = float(ds)
+    return out
