@@ -175,6 +175,62 @@ def decode_bench(args, torch, fa, dev):
     print(json.dumps(line), flush=True)
 
 
+def fp8_bench(args, torch, fa, dev, cfg):
+    """Forward only, FP8 (E4M3) Q, K, V with per-tensor descales (fa_fwd_fp8), on the
+    workload's shape and mask, next to the bf16 forward on the same shape.  FLOPs as
+    for the bf16 forward; peak = the dense 8-bit matrix rate, twice the bf16 one."""
+    B, H, N, d = cfg.shape()
+    if d != 128:
+        log("bench.py: the FP8 forward supports d = 128 only")
+        sys.exit(2)
+    inp = synth.draw_inputs_fp8(B, H, N, d, cfg.seed)
+    q8, k8, v8 = (torch.from_numpy(inp[x]).to(dev) for x in ("q", "k", "v"))
+    bits = synth.draw_inputs(B, H, N, d, cfg.seed, with_do=False)
+    q, k, v = (torch.from_numpy(bits[x].view(np.int16)).to(dev).view(torch.bfloat16)
+               for x in ("q", "k", "v"))
+    bm = cfg.blockmask()
+    bmg = None if bm is None else torch.from_numpy(bm).to(dev)
+    s, causal, mb = cfg.scale, cfg.causal, cfg.mask_block
+    o = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    runs = {
+        "fp8": lambda: fa.forward_fp8(q8, k8, v8, inp["q_descale"], inp["k_descale"],
+                                      inp["v_descale"], s, causal, bmg, mb, out=o, lse=lse),
+        "bf16": lambda: fa.forward(q, k, v, s, causal, bmg, mb, out=o, lse=lse),
+    }
+    ms = {}
+    for name, fn in runs.items():
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms[name] = e0.elapsed_time(e1) / args.steps
+    flops = 4.0 * B * H * N * N * d * mask_fraction(cfg)
+    tf = {n: flops / (t * 1e-3) / 1e12 for n, t in ms.items()}
+    peak8 = 2 * PEAK_BF16_TFLOPS
+    log(f"[bench] FP8 forward {cfg.name}: {ms['fp8'] * 1e3:.1f} us = {tf['fp8']:.0f} TFLOP/s; "
+        f"bf16 forward {ms['bf16'] * 1e3:.1f} us = {tf['bf16']:.0f} TFLOP/s")
+    line = {
+        "metric": "attention fwd TFLOP/s, FP8 E4M3 Q/K/V with per-tensor descales",
+        "value": tf["fp8"], "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms["fp8"], "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "fp8_e4m3", "data": "synthetic",
+        "config": {"workload": f"{cfg.name}: B={B} H={H} N={N} d={d} {cfg.mask}, forward only, "
+                               "FP8 inputs (descale = max|x| / 448)",
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": tf["fp8"], "peak": peak8, "unit": "TFLOP/s",
+                     "frac": tf["fp8"] / peak8, "traffic": None},
+        "bf16_forward_TFLOPs": tf["bf16"],
+        "kernel_source_hash": kernel_source_hash(),
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -188,6 +244,9 @@ def main():
                     help="instead of the training step, time one decoding step: B=8 H=16, one "
                          "query row per head against an NK-key cache (d=128, causal), "
                          "split-KV forward and the unsplit forward, as HBM GB/s of K and V")
+    ap.add_argument("--fp8", action="store_true",
+                    help="instead of the training step, time the FP8 forward (fa_fwd_fp8) on "
+                         "the workload's shape, next to the bf16 forward (d=128 workloads)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the oracle timed on host cores (0 disables it)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -220,6 +279,8 @@ def main():
     if args.decode > 0:
         return decode_bench(args, torch, fa, dev)
     cfg = synth.CONFIGS[args.workload]
+    if args.fp8:
+        return fp8_bench(args, torch, fa, dev, cfg)
     B, H, N, d = cfg.shape()
     bits = synth.config_inputs(cfg)
 

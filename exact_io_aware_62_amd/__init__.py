@@ -58,6 +58,8 @@ _SIGNATURES = {
                             _vp, _vp, _vp]),
     "fa_fwd_splitkv_num_splits": (_i, [_i, _i, _i, _i, _i]),
     "fa_fwd_splitkv_workspace_bytes": (_sz, [_i, _i, _i, _i, _i, _i]),
+    "fa_fwd_fp8": (_i, [_vp, _vp, _vp, _i, _i, _i, _i, _f, _f, _f, _f, _i, _vp, _i, _vp, _vp,
+                        _vp]),
     "fa_strerror": (ctypes.c_char_p, [_i]),
 }
 
@@ -428,3 +430,38 @@ def forward_splitkv(q, k, v, scale: float | None = None, causal: bool = False, b
         raise LibfaError(rc, "fa_fwd_splitkv")
     return out, lse
 
+
+
+def forward_fp8(q, k, v, q_descale: float, k_descale: float, v_descale: float,
+                scale: float | None = None, causal: bool = False, blockmask=None,
+                mask_block: int = 128, out=None, lse=None):
+    """FP8 forward (fa_fwd_fp8).  q, k, v: [B, H, N, 128] E4M3 codes, as
+    torch.float8_e4m3fn or torch.uint8 tensors; element x stands for
+    value(x) * descale of its tensor.  Returns (o bf16, lse fp32)."""
+    torch = _torch()
+    codes = (torch.float8_e4m3fn, torch.uint8)
+    if not isinstance(q, torch.Tensor) or q.dim() != 4:
+        raise ValueError("q must be a [B, H, N, d] tensor")
+    if q.dtype not in codes:
+        raise TypeError(f"q must be float8_e4m3fn or uint8 codes, got {q.dtype}")
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _check(t, name, q.dtype, (B, H, N, d), dev)
+    scale = default_scale(d) if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, H, N, d), dtype=torch.bfloat16, device=dev)
+    else:
+        _check(out, "out", torch.bfloat16, (B, H, N, d), dev)
+    if lse is None:
+        lse = torch.empty((B, H, N), dtype=torch.float32, device=dev)
+    else:
+        _check(lse, "lse", torch.float32, (B, H, N), dev)
+    bm_ptr, mb = _mask_args(blockmask, N, mask_block, dev)
+    rc = load_library().fa_fwd_fp8(q.data_ptr(), k.data_ptr(), v.data_ptr(), B, H, N, d, scale,
+                                   float(q_descale), float(k_descale), float(v_descale),
+                                   int(bool(causal)), bm_ptr, mb, out.data_ptr(),
+                                   lse.data_ptr(), _stream_ptr(dev))
+    if rc != FA_OK:
+        raise LibfaError(rc, "fa_fwd_fp8")
+    return out, lse

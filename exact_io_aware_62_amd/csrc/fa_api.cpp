@@ -173,6 +173,7 @@ int fwd_impl(const void* Q, const void* K, const void* V, int B, int H, int Nq, 
   p.mask_block = blockmask ? mask_block : 128;
   p.nbm = (Nk + p.mask_block - 1) / p.mask_block;
   p.scale_log2 = scale * kLog2e;
+  p.v_descale = 1.f;
   set_dropout(p, p_drop, seed, offset);
   p.nsplit = 1;
   p.tiles_per_split = 0;
@@ -257,6 +258,44 @@ int fa_fwd_dropout(const void* Q, const void* K, const void* V, int B, int H, in
                    hipStream_t stream) {
   return fwd_impl(Q, K, V, B, H, N, N, d, scale, causal, blockmask, mask_block, p_drop, seed,
                   offset, O, LSE, stream);
+}
+
+int fa_fwd_fp8(const void* Q, const void* K, const void* V, int B, int H, int N, int d,
+               float scale, float q_descale, float k_descale, float v_descale, int causal,
+               const uint8_t* blockmask, int mask_block, void* O, float* LSE,
+               hipStream_t stream) {
+  bool empty = false;
+  int rc = check_common(B, H, N, d, scale, blockmask, mask_block, &empty);
+  if (rc != FA_OK) return rc;
+  if (d != 128) return FA_ERR_UNSUPPORTED;
+  for (const float x : {q_descale, k_descale, v_descale})
+    if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_UNSUPPORTED;
+  // the folded score factor must stay a finite, nonzero fp32 number
+  const double c = (double)scale * q_descale * k_descale * 1.4426950408889634;
+  if (!(c > 1e-30 && c < 1e30)) return FA_ERR_UNSUPPORTED;
+  if (empty) return FA_OK;
+  if (!Q || !K || !V || !O || !LSE) return FA_ERR_NULL;
+  if (!all_aligned16({Q, K, V, O}) || !aligned(LSE, 4)) return FA_ERR_UNSUPPORTED;
+
+  fa::FwdParams p;
+  p.Q = static_cast<const uint16_t*>(Q);
+  p.K = static_cast<const uint16_t*>(K);
+  p.V = static_cast<const uint16_t*>(V);
+  p.O = static_cast<uint16_t*>(O);
+  p.LSE = LSE;
+  p.blockmask = blockmask;
+  p.BH = B * H;
+  p.Nq = p.Nk = N;
+  p.nqb = (N + 127) / 128;
+  p.mask_block = blockmask ? mask_block : 128;
+  p.nbm = (N + p.mask_block - 1) / p.mask_block;
+  p.scale_log2 = (float)c;
+  p.v_descale = v_descale;
+  set_dropout(p, 0.f, 0, 0);
+  p.nsplit = 1;
+  p.tiles_per_split = 0;
+  p.Opart = p.LSEpart = nullptr;
+  return status_of(fa::launch_fwd_fp8(p, d, causal != 0, blockmask != nullptr, stream));
 }
 
 size_t fa_bwd_workspace_bytes(int B, int H, int N, int d) {

@@ -19,7 +19,8 @@ struct FwdParams {
   int nqb;                   // ceil(Nq / 128) query blocks
   int mask_block;            // block-mask granularity (multiple of 128)
   int nbm;                   // ceil(Nk / mask_block): row stride of the block mask
-  float scale_log2;          // scale * log2(e)
+  float scale_log2;          // scale * log2(e) (FP8: scale * q_descale * k_descale * log2(e))
+  float v_descale;           // FP8: factor of every V element (1 otherwise)
   // split-KV (nsplit > 1): partial results [nsplit][BH][Nq][D] and [nsplit][BH][Nq]
   int nsplit, tiles_per_split;
   float* Opart;
@@ -62,6 +63,9 @@ struct BwdParams {
 // otherwise p.nsplit > 1 selects split-KV (p.Opart / p.LSEpart) plus the merge
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool sparse, bool dropout,
                       hipStream_t stream);
+// FP8 forward (E4M3 Q, K, V; p.scale_log2 and p.v_descale carry the descales); d = 128
+hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, bool sparse,
+                          hipStream_t stream);
 // keep[bh][i][j] (uint8) of the dropout stream set in p (BH, Nq, Nk, drop_*, seed_*)
 hipError_t launch_dropout_keep_mask(const FwdParams& p, uint8_t* keep, hipStream_t stream);
 hipError_t launch_bwd_dsum(const BwdParams& p, int d, hipStream_t stream);

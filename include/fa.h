@@ -277,6 +277,32 @@ int fa_bwd_dropout(const void* Q, const void* K, const void* V, const void* O,
 int fa_dropout_keep_mask(int B, int H, int N, float p_drop, uint64_t seed,
                          uint32_t offset, uint8_t* keep, hipStream_t stream);
 
+/*
+ * FP8 forward.  The FlashAttention-2 wiki ("与后续版本的比较",
+ * FlashAttention-3) names 8-bit floating point as the following generation's
+ * route to more speed; it fixes no format or scaling.  Here Q, K and V are
+ * [B,H,N,d] arrays of one-byte E4M3 codes (OCP 8-bit floating point, the
+ * variant without infinities: sign, 4 exponent bits with bias 7, 3 mantissa
+ * bits; max 448), DEVICE pointers, 16-byte aligned.  Element x of Q stands for
+ * value(x) * q_descale, and likewise for K and V with their own fp32 factor.
+ *
+ *   O   = softmax(scale * Q K^T + mask) V of those values, bf16 [B,H,N,d];
+ *   LSE = natural-log row log-sum-exp of the scaled, masked scores, fp32.
+ *
+ * Both products run on the 8-bit matrix cores with fp32 accumulation; P is
+ * rounded to E4M3 (nearest even) before the P V product, which moves each
+ * element of O by at most 2^-4 sum_j P_ij |v_j| + 2^-14 sum_j |v_j| (visible
+ * j) plus bf16 output rounding; LSE is formed from the unrounded fp32 P.
+ * Masks, N (any N >= 0) and errors as fa_fwd; d must be 128, and the three
+ * descales finite and > 0 (else FA_ERR_UNSUPPORTED).  Codes 0x7F / 0xFF (NaN)
+ * give undefined results.
+ */
+int fa_fwd_fp8(const void* Q, const void* K, const void* V,
+               int B, int H, int N, int d, float scale,
+               float q_descale, float k_descale, float v_descale, int causal,
+               const uint8_t* blockmask, int mask_block,
+               void* O, float* LSE, hipStream_t stream);
+
 /* Static, human-readable text for a status code (never NULL). */
 const char* fa_strerror(int status);
 

@@ -27,7 +27,8 @@ def test_exports_every_declared_symbol(lib):
                           "fa_bwd_dsum", "fa_bwd_dkdv", "fa_bwd_dq", "fa_bwd_dq_dsum",
                           "fa_fwd_dropout", "fa_bwd_dropout", "fa_dropout_keep_mask",
                           "fa_fwd_nqk", "fa_bwd_nqk", "fa_fwd_splitkv",
-                          "fa_fwd_splitkv_num_splits", "fa_fwd_splitkv_workspace_bytes"}
+                          "fa_fwd_splitkv_num_splits", "fa_fwd_splitkv_workspace_bytes",
+                          "fa_fwd_fp8"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -241,3 +242,28 @@ def test_splitkv_sizing_and_validation(lib):
     assert call(d=48) == fa.FA_ERR_UNSUPPORTED
     assert call(Nq=-1) == fa.FA_ERR_SHAPE
     assert call(Nq=0) == fa.FA_OK
+
+
+def fwd8(lib, q=FAKE, k=FAKE, v=FAKE, B=1, H=1, N=128, d=128, scale=0.088, qd=0.01, kd=0.02,
+         vd=0.03, causal=0, bm=None, mb=0, o=FAKE, lse=FAKE):
+    return lib.fa_fwd_fp8(q, k, v, B, H, N, d, scale, qd, kd, vd, causal, bm, mb, o, lse, None)
+
+
+def test_fp8_validation(lib):
+    assert fwd8(lib, B=-1) == fa.FA_ERR_SHAPE
+    assert fwd8(lib, d=64) == fa.FA_ERR_UNSUPPORTED        # FP8 path: d = 128 only
+    assert fwd8(lib, d=80) == fa.FA_ERR_UNSUPPORTED
+    assert fwd8(lib, scale=0.0) == fa.FA_ERR_UNSUPPORTED
+    for bad in (0.0, -1.0, math.inf, math.nan):
+        assert fwd8(lib, qd=bad) == fa.FA_ERR_UNSUPPORTED
+        assert fwd8(lib, kd=bad) == fa.FA_ERR_UNSUPPORTED
+        assert fwd8(lib, vd=bad) == fa.FA_ERR_UNSUPPORTED
+    # the folded score factor scale * q_descale * k_descale must stay a normal fp32 number
+    assert fwd8(lib, qd=1e-20, kd=1e-20) == fa.FA_ERR_UNSUPPORTED
+    assert fwd8(lib, qd=1e20, kd=1e20) == fa.FA_ERR_UNSUPPORTED
+    assert fwd8(lib, bm=FAKE, mb=64) == fa.FA_ERR_UNSUPPORTED
+    assert fwd8(lib, o=None) == fa.FA_ERR_NULL
+    assert fwd8(lib, k=None) == fa.FA_ERR_NULL
+    assert fwd8(lib, v=FAKE + 8) == fa.FA_ERR_UNSUPPORTED
+    assert fwd8(lib, lse=FAKE + 2) == fa.FA_ERR_UNSUPPORTED
+    assert fwd8(lib, N=0, q=None, k=None, v=None, o=None, lse=None) == fa.FA_OK

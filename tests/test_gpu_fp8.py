@@ -1,0 +1,221 @@
+"""GPU parity of the FP8 forward (fa_fwd_fp8) against the fp64 oracle.
+
+The oracle is exact attention of the dequantised E4M3 inputs.  The kernel also
+rounds P to E4M3 (nearest even) before the P V product, so O is checked against
+the bound that rounding implies (derived from E4M3's spacing: each P value moves
+by at most 2^-4 of itself, or by 2^-10 below 2^-6; the kernel's P values carry
+a factor 2^4 relative to the row sum, see fa.h), element by element:
+
+    |O - O_ref| <= 2^-4 sum_j P_ij |v_jc| + 2^-14 sum_j |v_jc| + 2^-8 |O_ref| + 1e-4 max|O_ref|
+
+(sums over visible keys; the third term is bf16 output rounding, the last fp32
+accumulation), plus a whole-tensor relative RMS error <= 0.035 (the rounding model
+predicts 0.020-0.026 on these inputs).  LSE comes from the unrounded fp32 P and
+keeps the bf16 path's tolerance: |LSE - LSE_ref| <= 1e-3.  Inputs where P is
+exactly representable (all scores equal; one key far ahead of the rest) must
+match the oracle to bf16 rounding.
+"""
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import TOL_LSE, from_gpu, lse_err, mask_to_gpu, torch_mod
+
+pytestmark = pytest.mark.gpu
+
+RMS_TOL = 0.035
+
+
+@pytest.fixture(scope="module")
+def fa():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a GPU")
+    import exact_io_aware_62_amd as fa
+    fa.load_library()
+    return fa
+
+
+def codes_to_gpu(x):
+    torch = torch_mod()
+    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.uint8)).to("cuda:0")
+
+
+def run_fp8(fa, inp, scale, causal, bm=None, mb=128):
+    torch = torch_mod()
+    q, k, v = (codes_to_gpu(inp[n]) for n in ("q", "k", "v"))
+    o, lse = fa.forward_fp8(q, k, v, inp["q_descale"], inp["k_descale"], inp["v_descale"],
+                            scale, causal, mask_to_gpu(bm), mb)
+    torch.cuda.synchronize()
+    return from_gpu(o), lse.cpu().numpy().astype(np.float64)
+
+
+def ref_head(inp, b, h, scale, allowed):
+    return oracle.head_forward_fp8(inp["q"][b, h], inp["k"][b, h], inp["v"][b, h], scale,
+                                   inp["q_descale"], inp["k_descale"], inp["v_descale"], allowed)
+
+
+def check_head(o, lse, inp, b, h, scale, allowed, tag):
+    o_ref, lse_ref, p = ref_head(inp, b, h, scale, allowed)
+    v = np.abs(oracle.dequantize(inp["v"][b, h], inp["v_descale"]))
+    err = np.abs(o[b, h] - o_ref)
+    omax = np.abs(o_ref).max() if o_ref.size else 0.0
+    bound = 2.0 ** -4 * (p @ v) + 2.0 ** -14 * (allowed.astype(np.float64) @ v) \
+        + 2.0 ** -8 * np.abs(o_ref) + 1e-4 * omax
+    le = lse_err(lse[b, h], lse_ref)
+    den = np.sqrt((o_ref ** 2).sum())
+    rms = float(np.sqrt((err ** 2).sum()) / den) if den > 0 else float(np.sqrt((err ** 2).sum()))
+    worst = float((err / np.maximum(bound, 1e-300)).max()) if err.size else 0.0
+    print(f"{tag} head ({b},{h}): lse {le:.2e} rms {rms:.4f} err/bound {worst:.3f}", flush=True)
+    assert le <= TOL_LSE, le
+    assert np.all(err <= bound), worst
+    return rms, err, o_ref
+
+
+SMALL = [
+    # B, H, N, mask, seed
+    (1, 2, 128, "dense", 1),
+    (2, 2, 384, "dense", 2),
+    (2, 2, 448, "causal", 3),
+    (1, 2, 200, "dense", 4),           # ragged tail
+    (1, 3, 333, "causal", 5),          # ragged + causal
+    (1, 1, 1, "dense", 6),             # one token
+    (1, 1, 65, "causal", 7),
+    (1, 2, 512, "butterfly", 8),
+    (1, 2, 640, "random_holes", 9),    # empty block rows
+    (1, 1, 512, "random_holes_causal", 10),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[f"B{c[0]}H{c[1]}N{c[2]}-{c[3]}" for c in SMALL])
+def test_fp8_small(fa, case):
+    B, H, N, kind, seed = case
+    d = 128
+    rng = np.random.default_rng(seed)
+    causal = kind.endswith("causal")
+    nb = -(-N // 128)
+    bm = None
+    if kind == "butterfly":
+        bm = synth.butterfly_blockmask(nb)
+    elif kind.startswith("random_holes"):
+        bm = synth.make_blockmask("random_holes", nb, rng, 0.5)
+        bm[min(1, nb - 1)] = 0
+    inp = synth.draw_inputs_fp8(B, H, N, d, seed)
+    scale = float(np.float32(d ** -0.5))
+    o, lse = run_fp8(fa, inp, scale, causal, bm)
+    allowed = oracle.allowed_mask(N, N, causal, bm, 128)
+    num = den = 0.0
+    for b in range(B):
+        for h in range(H):
+            _, err, o_ref = check_head(o, lse, inp, b, h, scale, allowed, str(case))
+            num += (err ** 2).sum()
+            den += (o_ref ** 2).sum()
+    if N > 64:
+        assert np.sqrt(num / den) <= RMS_TOL
+    dead = ~allowed.any(1)
+    if dead.any():
+        assert np.all(o[:, :, dead] == 0)
+        assert np.all(lse[:, :, dead] == -np.inf)
+
+
+def test_fp8_full_size_causal_sampled(fa):
+    """B=8, H=16, N=2048, d=128, causal: the causal training shape in FP8,
+    three heads compared in full."""
+    B, H, N, d = 8, 16, 2048, 128
+    inp = synth.draw_inputs_fp8(B, H, N, d, 123)
+    scale = float(np.float32(d ** -0.5))
+    o, lse = run_fp8(fa, inp, scale, True)
+    allowed = oracle.allowed_mask(N, N, True)
+    for hh in (0, 77, B * H - 1):
+        b, h = divmod(hh, H)
+        rms, _, _ = check_head(o, lse, inp, b, h, scale, allowed, "C3-fp8")
+        assert rms <= RMS_TOL
+    assert np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+def test_fp8_full_size_dense_sampled(fa):
+    """B=2, H=16, N=4096, d=128, no mask: two heads compared in full."""
+    B, H, N, d = 2, 16, 4096, 128
+    inp = synth.draw_inputs_fp8(B, H, N, d, 321)
+    scale = float(np.float32(d ** -0.5))
+    o, lse = run_fp8(fa, inp, scale, False)
+    allowed = np.ones((N, N), bool)
+    for hh in (3, B * H - 1):
+        b, h = divmod(hh, H)
+        rms, _, _ = check_head(o, lse, inp, b, h, scale, allowed, "dense-fp8")
+        assert rms <= RMS_TOL
+
+
+def test_fp8_equal_scores_exact(fa):
+    """K = 0: every visible score is 0, P is the same exactly representable value
+    for every key, so O is the mean of the visible V rows times v_descale."""
+    B, H, N, d = 1, 2, 333, 128
+    inp = synth.draw_inputs_fp8(B, H, N, d, 17)
+    inp["k"][:] = 0
+    inp["v_descale"] = 0.0371
+    scale = float(np.float32(d ** -0.5))
+    for causal in (False, True):
+        o, lse = run_fp8(fa, inp, scale, causal)
+        allowed = oracle.allowed_mask(N, N, causal)
+        for h in range(H):
+            o_ref, lse_ref, _ = ref_head(inp, 0, h, scale, allowed)
+            assert np.abs(o[0, h] - o_ref).max() <= np.abs(o_ref).max() * 2.0 ** -8 + 1e-6
+            assert np.abs(lse[0, h] - lse_ref).max() <= 1e-5
+
+
+def _one_hot_inputs(N, causal, seed):
+    """Key j is the sum of two unit vectors (a pair unique to j) times 16; query i
+    is its winner's pair times 16.  The winner's score leads every other by at
+    least 16 * 16 * scale, about 33 in log2 units, so every other P value
+    rounds to 0 in E4M3 and the winner's is exact."""
+    d = 128
+    rng = np.random.default_rng(seed)
+    pairs = [(a, b) for a in range(d) for b in range(a + 1, d)]
+    sel = rng.choice(len(pairs), size=N, replace=False)
+    k = np.zeros((1, 1, N, d), np.uint8)
+    q = np.zeros((1, 1, N, d), np.uint8)
+    sixteen = synth.e4m3_round_codes(16.0)
+    for j, s in enumerate(sel):
+        a, b = pairs[s]
+        k[0, 0, j, a] = k[0, 0, j, b] = sixteen
+    win = np.array([rng.integers(0, i + 1) if causal else rng.integers(0, N) for i in range(N)])
+    q[0, 0] = k[0, 0, win]
+    v = synth.draw_inputs_fp8(1, 1, N, d, seed + 1)["v"]
+    return {"q": q, "k": k, "v": v, "q_descale": 1.0, "k_descale": 1.0,
+            "v_descale": 0.0123}, win
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_fp8_one_hot_exact(fa, causal):
+    N = 700
+    inp, win = _one_hot_inputs(N, causal, 5 + causal)
+    scale = float(np.float32(128 ** -0.5))
+    o, lse = run_fp8(fa, inp, scale, causal)
+    allowed = oracle.allowed_mask(N, N, causal)
+    o_ref, lse_ref, _ = ref_head(inp, 0, 0, scale, allowed)
+    vrow = oracle.dequantize(inp["v"][0, 0, win], inp["v_descale"])
+    assert np.abs(o_ref - vrow).max() <= 1e-6 * np.abs(vrow).max()
+    assert np.abs(o[0, 0] - o_ref).max() <= 2.0 ** -8 * np.abs(o_ref).max()
+    assert np.all(np.abs(o[0, 0] - o_ref) <= 2.0 ** -8 * np.abs(o_ref) + 1e-7)
+    assert np.abs(lse[0, 0] - lse_ref).max() <= 1e-3
+
+
+def test_fp8_bitwise_deterministic(fa):
+    inp = synth.draw_inputs_fp8(2, 4, 1024, 128, 44)
+    s = float(np.float32(128 ** -0.5))
+    o1, l1 = run_fp8(fa, inp, s, True)
+    o2, l2 = run_fp8(fa, inp, s, True)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
+def test_fp8_accepts_float8_dtype(fa):
+    torch = torch_mod()
+    inp = synth.draw_inputs_fp8(1, 2, 256, 128, 45)
+    s = float(np.float32(128 ** -0.5))
+    o1, l1 = run_fp8(fa, inp, s, False)
+    q, k, v = (codes_to_gpu(inp[n]).view(torch.float8_e4m3fn) for n in ("q", "k", "v"))
+    o2, l2 = fa.forward_fp8(q, k, v, inp["q_descale"], inp["k_descale"], inp["v_descale"], s)
+    torch.cuda.synchronize()
+    assert np.array_equal(o1, from_gpu(o2)) and np.array_equal(l1, l2.cpu().numpy())
