@@ -180,9 +180,6 @@ def fp8_bench(args, torch, fa, dev, cfg):
     workload's shape and mask, next to the bf16 forward on the same shape.  FLOPs as
     for the bf16 forward; peak = the dense 8-bit matrix rate, twice the bf16 one."""
     B, H, N, d = cfg.shape()
-    if d != 128:
-        log("bench.py: the FP8 forward supports d = 128 only")
-        sys.exit(2)
     inp = synth.draw_inputs_fp8(B, H, N, d, cfg.seed)
     q8, k8, v8 = (torch.from_numpy(inp[x]).to(dev) for x in ("q", "k", "v"))
     bits = synth.draw_inputs(B, H, N, d, cfg.seed, with_do=False)
@@ -246,7 +243,7 @@ def main():
                          "split-KV forward and the unsplit forward, as HBM GB/s of K and V")
     ap.add_argument("--fp8", action="store_true",
                     help="instead of the training step, time the FP8 forward (fa_fwd_fp8) on "
-                         "the workload's shape, next to the bf16 forward (d=128 workloads)")
+                         "the workload's shape, next to the bf16 forward")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the oracle timed on host cores (0 disables it)")
     ap.add_argument("--copy-calibration", action="store_true",

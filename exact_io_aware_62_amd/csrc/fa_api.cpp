@@ -267,7 +267,6 @@ int fa_fwd_fp8(const void* Q, const void* K, const void* V, int B, int H, int N,
   bool empty = false;
   int rc = check_common(B, H, N, d, scale, blockmask, mask_block, &empty);
   if (rc != FA_OK) return rc;
-  if (d != 128) return FA_ERR_UNSUPPORTED;
   for (const float x : {q_descale, k_descale, v_descale})
     if (!std::isfinite(x) || !(x > 0.f)) return FA_ERR_UNSUPPORTED;
   // the folded score factor must stay a finite, nonzero fp32 number

@@ -226,9 +226,11 @@ struct LaneOffsets {
 // or past `n_valid` are fetched from row n_valid - 1 instead (valid memory,
 // finite values); every kernel masks those rows, so they never contribute.
 // ---------------------------------------------------------------------------
+// D = 32 serves rows of 64 one-byte values (the FP8 kernel at head dim 64):
+// only the byte size of a row matters to the layout.
 template <int ROWS, int D>
 struct LdsTile {
-  static_assert(D == 64 || D == 128, "head dim");
+  static_assert(D == 32 || D == 64 || D == 128, "row size");
   static constexpr int kRows = ROWS;
   static constexpr int kD = D;
   static constexpr int kCPR = D / 8;                 // chunks per row
@@ -239,8 +241,10 @@ struct LdsTile {
   __device__ static __forceinline__ int swz(int row) {
     if constexpr (D == 128)
       return ((row & 3) << 2) | ((row >> 2) & 3);
-    else
+    else if constexpr (D == 64)
       return (((row >> 1) & 1) << 2) | ((row >> 2) & 3);
+    else
+      return (row >> 2) & 3;   // four chunks per row
   }
   // byte offset of logical 16-byte chunk `chunk` of row `row`
   __device__ static __forceinline__ int off(int row, int chunk) {

@@ -389,22 +389,29 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(FwdParams p) {
   }
 }
 
-hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, bool sparse,
-                          hipStream_t stream) {
-  if (d != 128) return hipErrorInvalidValue;
+template <int D>
+static hipError_t launch_fwd_fp8_t(const FwdParams& p, bool causal, bool sparse,
+                                   hipStream_t stream) {
   const dim3 grid((unsigned)((long long)p.nqb * p.BH));
   if (causal) {
     if (sparse)
-      hipLaunchKernelGGL((fwd_fp8_kernel<128, true, true>), grid, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, true, true>), grid, dim3(256), 0, stream, p);
     else
-      hipLaunchKernelGGL((fwd_fp8_kernel<128, true, false>), grid, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, true, false>), grid, dim3(256), 0, stream, p);
   } else {
     if (sparse)
-      hipLaunchKernelGGL((fwd_fp8_kernel<128, false, true>), grid, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, false, true>), grid, dim3(256), 0, stream, p);
     else
-      hipLaunchKernelGGL((fwd_fp8_kernel<128, false, false>), grid, dim3(256), 0, stream, p);
+      hipLaunchKernelGGL((fwd_fp8_kernel<D, false, false>), grid, dim3(256), 0, stream, p);
   }
   return hipGetLastError();
+}
+
+hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, bool sparse,
+                          hipStream_t stream) {
+  if (d == 64) return launch_fwd_fp8_t<64>(p, causal, sparse, stream);
+  if (d == 128) return launch_fwd_fp8_t<128>(p, causal, sparse, stream);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace fa

@@ -63,7 +63,7 @@ struct BwdParams {
 // otherwise p.nsplit > 1 selects split-KV (p.Opart / p.LSEpart) plus the merge
 hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool sparse, bool dropout,
                       hipStream_t stream);
-// FP8 forward (E4M3 Q, K, V; p.scale_log2 and p.v_descale carry the descales); d = 128
+// FP8 forward (E4M3 Q, K, V; p.scale_log2 and p.v_descale carry the descales); d = 64, 128
 hipError_t launch_fwd_fp8(const FwdParams& p, int d, bool causal, bool sparse,
                           hipStream_t stream);
 // keep[bh][i][j] (uint8) of the dropout stream set in p (BH, Nq, Nk, drop_*, seed_*)

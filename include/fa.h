@@ -293,8 +293,9 @@ int fa_dropout_keep_mask(int B, int H, int N, float p_drop, uint64_t seed,
  * rounded to E4M3 (nearest even) before the P V product, which moves each
  * element of O by at most 2^-4 sum_j P_ij |v_j| + 2^-14 sum_j |v_j| (visible
  * j) plus bf16 output rounding; LSE is formed from the unrounded fp32 P.
- * Masks, N (any N >= 0) and errors as fa_fwd; d must be 128, and the three
- * descales finite and > 0 (else FA_ERR_UNSUPPORTED).  Codes 0x7F / 0xFF (NaN)
+ * Masks, N (any N >= 0), d (64 or 128) and errors as fa_fwd; the three
+ * descales must be finite and > 0, and scale * q_descale * k_descale * log2(e)
+ * between 1e-30 and 1e30 (else FA_ERR_UNSUPPORTED).  Codes 0x7F / 0xFF (NaN)
  * give undefined results.
  */
 int fa_fwd_fp8(const void* Q, const void* K, const void* V,

@@ -251,7 +251,6 @@ def fwd8(lib, q=FAKE, k=FAKE, v=FAKE, B=1, H=1, N=128, d=128, scale=0.088, qd=0.
 
 def test_fp8_validation(lib):
     assert fwd8(lib, B=-1) == fa.FA_ERR_SHAPE
-    assert fwd8(lib, d=64) == fa.FA_ERR_UNSUPPORTED        # FP8 path: d = 128 only
     assert fwd8(lib, d=80) == fa.FA_ERR_UNSUPPORTED
     assert fwd8(lib, scale=0.0) == fa.FA_ERR_UNSUPPORTED
     for bad in (0.0, -1.0, math.inf, math.nan):

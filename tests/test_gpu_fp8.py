@@ -75,24 +75,31 @@ def check_head(o, lse, inp, b, h, scale, allowed, tag):
 
 
 SMALL = [
-    # B, H, N, mask, seed
-    (1, 2, 128, "dense", 1),
-    (2, 2, 384, "dense", 2),
-    (2, 2, 448, "causal", 3),
-    (1, 2, 200, "dense", 4),           # ragged tail
-    (1, 3, 333, "causal", 5),          # ragged + causal
-    (1, 1, 1, "dense", 6),             # one token
-    (1, 1, 65, "causal", 7),
-    (1, 2, 512, "butterfly", 8),
-    (1, 2, 640, "random_holes", 9),    # empty block rows
-    (1, 1, 512, "random_holes_causal", 10),
+    # B, H, N, d, mask, seed
+    (1, 2, 128, 128, "dense", 1),
+    (2, 2, 384, 128, "dense", 2),
+    (2, 2, 448, 128, "causal", 3),
+    (1, 2, 200, 128, "dense", 4),           # ragged tail
+    (1, 3, 333, 128, "causal", 5),          # ragged + causal
+    (1, 1, 1, 128, "dense", 6),             # one token
+    (1, 1, 65, 128, "causal", 7),
+    (1, 2, 512, 128, "butterfly", 8),
+    (1, 2, 640, 128, "random_holes", 9),    # empty block rows
+    (1, 1, 512, 128, "random_holes_causal", 10),
+    (1, 2, 128, 64, "dense", 11),
+    (2, 2, 448, 64, "causal", 12),
+    (1, 2, 200, 64, "dense", 13),
+    (1, 3, 333, 64, "causal", 14),
+    (1, 1, 1, 64, "causal", 15),
+    (1, 2, 512, 64, "butterfly", 16),
+    (1, 2, 640, 64, "random_holes_causal", 17),
 ]
 
 
-@pytest.mark.parametrize("case", SMALL, ids=[f"B{c[0]}H{c[1]}N{c[2]}-{c[3]}" for c in SMALL])
+@pytest.mark.parametrize("case", SMALL,
+                         ids=[f"B{c[0]}H{c[1]}N{c[2]}d{c[3]}-{c[4]}" for c in SMALL])
 def test_fp8_small(fa, case):
-    B, H, N, kind, seed = case
-    d = 128
+    B, H, N, d, kind, seed = case
     rng = np.random.default_rng(seed)
     causal = kind.endswith("causal")
     nb = -(-N // 128)
@@ -148,11 +155,29 @@ def test_fp8_full_size_dense_sampled(fa):
         assert rms <= RMS_TOL
 
 
-def test_fp8_equal_scores_exact(fa):
+def test_fp8_full_size_d64_sampled(fa):
+    """B=64, H=16, N=1024, d=64, no mask (the digest's micro-benchmark shape) and
+    B=4, H=16, N=4096, d=64 with the butterfly block mask: sampled heads."""
+    for (B, H, N, kind, seed) in ((64, 16, 1024, "dense", 501), (4, 16, 4096, "butterfly", 502)):
+        d = 64
+        inp = synth.draw_inputs_fp8(B, H, N, d, seed)
+        scale = float(np.float32(d ** -0.5))
+        bm = synth.butterfly_blockmask(N // 128) if kind == "butterfly" else None
+        o, lse = run_fp8(fa, inp, scale, False, bm)
+        allowed = oracle.allowed_mask(N, N, False, bm, 128)
+        for hh in (0, B * H // 2 + 3, B * H - 1):
+            b, h = divmod(hh, H)
+            rms, _, _ = check_head(o, lse, inp, b, h, scale, allowed, f"{kind}-d64-fp8")
+            assert rms <= RMS_TOL
+        assert np.isfinite(o).all() and np.isfinite(lse).all()
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_equal_scores_exact(fa, d):
     """K = 0: every visible score is 0, P is the same exactly representable value
     for every key, so O is the mean of the visible V rows times v_descale."""
-    B, H, N, d = 1, 2, 333, 128
-    inp = synth.draw_inputs_fp8(B, H, N, d, 17)
+    B, H, N = 1, 2, 333
+    inp = synth.draw_inputs_fp8(B, H, N, d, 17 + d)
     inp["k"][:] = 0
     inp["v_descale"] = 0.0371
     scale = float(np.float32(d ** -0.5))
@@ -165,12 +190,11 @@ def test_fp8_equal_scores_exact(fa):
             assert np.abs(lse[0, h] - lse_ref).max() <= 1e-5
 
 
-def _one_hot_inputs(N, causal, seed):
+def _one_hot_inputs(N, causal, seed, d=128):
     """Key j is the sum of two unit vectors (a pair unique to j) times 16; query i
     is its winner's pair times 16.  The winner's score leads every other by at
-    least 16 * 16 * scale, about 33 in log2 units, so every other P value
-    rounds to 0 in E4M3 and the winner's is exact."""
-    d = 128
+    least 16 * 16 * scale (about 33 in log2 units at d = 128, 46 at d = 64), so
+    every other P value rounds to 0 in E4M3 and the winner's is exact."""
     rng = np.random.default_rng(seed)
     pairs = [(a, b) for a in range(d) for b in range(a + 1, d)]
     sel = rng.choice(len(pairs), size=N, replace=False)
@@ -187,11 +211,12 @@ def _one_hot_inputs(N, causal, seed):
             "v_descale": 0.0123}, win
 
 
+@pytest.mark.parametrize("d", [64, 128])
 @pytest.mark.parametrize("causal", [False, True])
-def test_fp8_one_hot_exact(fa, causal):
+def test_fp8_one_hot_exact(fa, causal, d):
     N = 700
-    inp, win = _one_hot_inputs(N, causal, 5 + causal)
-    scale = float(np.float32(128 ** -0.5))
+    inp, win = _one_hot_inputs(N, causal, 5 + causal, d)
+    scale = float(np.float32(d ** -0.5))
     o, lse = run_fp8(fa, inp, scale, causal)
     allowed = oracle.allowed_mask(N, N, causal)
     o_ref, lse_ref, _ = ref_head(inp, 0, 0, scale, allowed)

@@ -73,3 +73,71 @@ def test_transposed_reads_conflict_free(D):
                     a = tr_offset(D, db * 32, lane, half)
                     banks |= {(a // 4 + i) % 64 for i in range(2)}
                 assert len(banks) == 64, (D, db, half, lo)
+
+
+# ---------------------------------------------------------------------------
+# FP8 tiles: rows of d one-byte codes, stored in the format of d/2 two-byte
+# values (row bytes RB = d; RB = 64 uses swz(row) = (row >> 2) & 3).
+# ---------------------------------------------------------------------------
+
+def swz_bytes(RB, row):
+    if RB == 64:
+        return (row >> 2) & 3
+    return swz(RB // 2, row)
+
+
+def off_bytes(RB, row, chunk):
+    return row * RB + ((chunk ^ swz_bytes(RB, row)) << 4)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_score_operand_reads_conflict_free(d):
+    # K rows for the 8-bit score product j = kb + 2 kk: lane (r, g) reads row
+    # 32 kb + r, chunks 4 kk + 2 g + h with two ds_read_b128 (h = 0, 1); the
+    # kernel forms the address as row base + ((4 kk + h) ^ ((2 g) ^ swz(r))) << 4
+    for kk in range(d // 64):
+        for kb in range(2):
+            for h in range(2):
+                for lo in range(0, 64, 16):
+                    banks = set()
+                    for lane in range(lo, lo + 16):
+                        r, g = lane & 31, lane >> 5
+                        a = off_bytes(d, 32 * kb + r, 4 * kk + 2 * g + h)
+                        short = (32 * kb + r) * d + (((4 * kk + h) ^ ((2 * g) ^ swz_bytes(d, r))) << 4)
+                        assert a == short
+                        banks |= {(a // 4 + i) % 64 for i in range(4)}
+                    assert len(banks) == 64, (d, kk, kb, h, lo)
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_fp8_transposed_value_reads(d):
+    # ds_read_b64_tr_b8 for output block db, read t: the lane pair 2e, 2e+1 of a
+    # 16-lane group addresses row 32 (t/2) + 16 (t%2) + 8 (e/4) + 4 g + e%4,
+    # bytes 32 db + 16 gi + 8 (lane % 2) .. +7.  Checks: the kernel's short
+    # address form, the rows each lane receives (the keys of P's register order),
+    # and no bank conflict among the 32 lanes served per cycle.
+    for db in range(d // 32):
+        for t in range(4):
+            for lo in (0, 32):
+                banks = set()
+                for lane in range(lo, lo + 32):
+                    s16, gi, g = lane & 15, (lane >> 4) & 1, lane >> 5
+                    e = s16 >> 1
+                    vrl = 8 * (e >> 2) + 4 * g + (e & 3)
+                    R = 32 * (t >> 1) + 16 * (t & 1) + vrl
+                    col = 32 * db + 16 * gi + 8 * (s16 & 1)
+                    a = off_bytes(d, R, col >> 4) + (col & 15)
+                    short = (32 * (t >> 1) + 16 * (t & 1)) * d + vrl * d + 8 * (s16 & 1) \
+                        + ((db << 5) ^ ((gi ^ swz_bytes(d, vrl)) << 4))
+                    assert a == short
+                    banks |= {(a // 4 + i) % 64 for i in range(2)}
+                assert len(banks) == 64, (d, db, t, lo)
+    # received rows: lane l of 16-lane group gets byte l % 8 of the piece of lane
+    # 2e + l / 8, i.e. column col0 + l, rows R(e) for e = 0..7; byte j = 8 t + e of
+    # lane group g must be key 32 (j / 16) + 8 ((j % 16) / 4) + 4 g + j % 4
+    for g in range(2):
+        for t in range(4):
+            for e in range(8):
+                j = 8 * t + e
+                R = 32 * (t >> 1) + 16 * (t & 1) + 8 * (e >> 2) + 4 * g + (e & 3)
+                assert R == 32 * (j // 16) + 8 * ((j % 16) // 4) + 4 * g + j % 4
