@@ -342,7 +342,9 @@ __global__ __launch_bounds__(256, (DROPOUT && D == 128) ? 1 : 2) void dkdv_kerne
     const int tn = next_tile(t + 1);
     if (tn < nqt) issue(tn, stage ^ 1);
     if constexpr (DROPOUT) keep_cur = keep_next;
-    compute(stage, t, tn);
+    // a query tile entirely before this wavefront's first key's diagonal
+    // contributes 0 (the dropout form draws the next tile's bits in there)
+    if (DROPOUT || !(CAUSAL && t * BQ + BQ - 1 + dlt < kw)) compute(stage, t, tn);
     if (tn < nqt) finish_issue(stage ^ 1);
     t = tn;
     stage ^= 1;
