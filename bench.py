@@ -30,6 +30,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -50,12 +51,22 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def _code_only(text: str) -> str:
+    """C/C++ source without comments and with whitespace runs collapsed, so that a
+    change of comments or layout alone keeps the hash (string literals in these
+    sources hold no comment markers)."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash() -> str:
+    """Hash of the code (not the comments) of every kernel and host source file."""
     h = hashlib.sha256()
     for path in sorted(glob.glob(os.path.join(ROOT, "exact_io_aware_62_amd", "csrc", "*"))):
-        with open(path, "rb") as f:
+        with open(path, encoding="utf-8") as f:
             h.update(os.path.basename(path).encode())
-            h.update(f.read())
+            h.update(_code_only(f.read()).encode())
     return h.hexdigest()[:16]
 
 

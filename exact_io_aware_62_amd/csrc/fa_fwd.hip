@@ -27,14 +27,17 @@
 // same wavefront can issue independent vector ops; the exp2 work of the
 // softmax (about half the matrix time at d = 128) therefore hides behind
 // matrix work only if the two are interleaved in one instruction stream.
-// Iteration i holds the scores S_i of tile i (computed in iteration i-1):
-//   phase 1  mask S_i if the tile needs it, row max, rare rescale of O;
-//   phase 2  S_{i+1} = K_{i+1} Q^T on the matrix cores, interleaved with
-//            P_i = exp2(S_i c - m) and its bf16 packing;
-//   phase 3  O^T += V_i^T P_i^T, interleaved with the row sum of P_i and
-//            the row max of S_{i+1}.
-// Masked tiles (causal diagonal, ragged end) are always the last tiles of
-// a row block, so masking stays in phase 1 outside the interleaved code.
+// Iteration i (tile i, K_i in LDS, V_{i-1} and the packed P_{i-1} held over
+// from iteration i-1):
+//   phase A  S_i^T = K_i Q^T on the matrix cores (operands read ahead);
+//            then the mask, if the tile needs one;
+//   phase B  O^T += V_{i-1}^T P_{i-1}^T on the matrix cores, interleaved with
+//            tile i's softmax: its row max under the first two products,
+//            then P_i = exp2(S_i c - m), the fp32 row sum and the bf16
+//            packing of P_i under the rest; then the rare rescale of O.
+// The last tile's P V product runs alone after the loop.  Masked tiles
+// (causal diagonal, ragged end) are the last tiles of a row block, so the
+// mask branch sits between the phases, outside the interleaved code.
 
 #include <type_traits>
 
