@@ -324,7 +324,8 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
     }
   };
 
-  int t = next_tile(t_begin);
+  const int t_first = next_tile(t_begin);
+  int t = t_first;
   int stage = 0;
   if (t < nqt) {
     issue(t, 0);
@@ -350,24 +351,18 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
     stage ^= 1;
   }
 
-  // epilogue: lane owns key `key`; register i of block db is column
-  // db*32 + (i/4)*8 + g*4 + i%4
-  if (key < Nk) {
-    uint16_t* dKh = p.dK + khead + (size_t)key * D;
-    uint16_t* dVh = p.dV + khead + (size_t)key * D;
-    const float sc = p.scale;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const int col = db * 32 + qd * 8 + g * 4;
-        *reinterpret_cast<u32x2*>(dVh + col) =
-            pack_bf16x4(dv[db][qd * 4 + 0], dv[db][qd * 4 + 1], dv[db][qd * 4 + 2],
-                        dv[db][qd * 4 + 3]);
-        *reinterpret_cast<u32x2*>(dKh + col) =
-            pack_bf16x4(dk[db][qd * 4 + 0] * sc, dk[db][qd * 4 + 1] * sc, dk[db][qd * 4 + 2] * sc,
-                        dk[db][qd * 4 + 3] * sc);
-      }
+  // epilogue: dV and dK (lane r + 32 g holds key kw + r) leave through this
+  // wavefront's own 32 rows of the K buffer, which no other wavefront reads.
+  // Without a single query tile the K copy was never waited for: wait for
+  // it (every wavefront fills part of every row block) before overwriting.
+  if (t_first >= nqt) {
+    wait_vmem();
+    __syncthreads();
+  }
+  if (kw < Nk) {
+    char* stage = kbuf + wave * 32 * RB;
+    store_rows_staged<D>(stage, dv, 1.f, p.dV + khead + (size_t)kw * D, Nk - kw, lane);
+    store_rows_staged<D>(stage, dk, p.scale, p.dK + khead + (size_t)kw * D, Nk - kw, lane);
   }
 }
 
@@ -601,7 +596,17 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     stage ^= 1;
   }
 
-  if (qrow < Nq) {
+  // dQ leaves through the stage the loop did not end on: every wavefront
+  // passed the barrier of the last tile, so none reads it, and no copy into
+  // it is outstanding.  Rows 32 w .. 32 w + 31 of its K tile (w = 0, 1) or V
+  // tile (w = 2, 3) serve wavefront w.  Block-sparse grids store straight
+  // from the accumulator layout, which measured faster there.
+  if constexpr (!SPARSE) {
+    if (q0w < Nq) {
+      char* st = (wave < 2 ? kbuf : vbuf) + stage * T::kBytes + (wave & 1) * 32 * RB;
+      store_rows_staged<D>(st, dq, p.scale, p.dQ + qhead + (size_t)q0w * D, Nq - q0w, lane);
+    }
+  } else if (qrow < Nq) {
     uint16_t* dQh = p.dQ + qhead + (size_t)qrow * D;
     const float sc = p.scale;
 #pragma unroll

@@ -402,6 +402,58 @@ __device__ __forceinline__ OperandAddr<T> operand_addr(int lane) {
   return o;
 }
 
+// Writes a wavefront's 32 output rows of D bf16 values, held in the 32x32
+// accumulator layout (lane r + 32 g holds row r; register qd*4 + e of column
+// block db is column db*32 + qd*8 + g*4 + e), times `mul`, to rows
+// dst[0 .. valid) of a row-major global array with row stride D.
+//
+// Written straight from that layout, one store instruction touches 32 rows
+// with 16 bytes each.  Instead the values go through `stage`, an LDS area of
+// 32 * 2D bytes that only this wavefront uses: each lane writes its 8-byte
+// pieces, then reads back 16 consecutive bytes of one row, so that a store
+// instruction covers 64 / (D/8) whole consecutive rows.  The 16-byte chunks
+// of a staged row are XOR-swizzled by the index of the row's 256-byte bank
+// line (the row itself at D = 128, row / 2 at D = 64, where two rows share
+// the 64 banks), which spreads both the writes and the row reads over all
+// LDS banks.  The caller guarantees that no
+// other wavefront touches `stage` meanwhile and that no copy into it is
+// outstanding.
+template <int D>
+__device__ __forceinline__ void store_rows_staged(char* stage, const f32x16 (&acc)[D / 32],
+                                                  float mul, uint16_t* dst, int valid, int lane) {
+  constexpr int NDB = D / 32, CPR = D / 8, RB = 2 * D, RPI = 64 / CPR, SH = D == 64 ? 1 : 0;
+  const int r = lane & 31, g = lane >> 5;
+#pragma unroll
+  for (int db = 0; db < NDB; ++db)
+#pragma unroll
+    for (int qd = 0; qd < 4; ++qd)
+      *reinterpret_cast<u32x2*>(stage + r * RB + (((db * 4 + qd) ^ ((r >> SH) & (CPR - 1))) << 4) +
+                                g * 8) =
+          pack_bf16x4(acc[db][qd * 4 + 0] * mul, acc[db][qd * 4 + 1] * mul,
+                      acc[db][qd * 4 + 2] * mul, acc[db][qd * 4 + 3] * mul);
+  // the reads below take values other lanes wrote: keep them after the writes
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+  constexpr int NI = 32 / RPI;
+  const int ch = lane % CPR, row0 = lane / CPR;
+  u32x4 v[NI];
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int row = i * RPI + row0;
+    v[i] = *reinterpret_cast<const u32x4*>(stage + row * RB + ((ch ^ ((row >> SH) & (CPR - 1))) << 4));
+  }
+  uint16_t* d0 = dst + (size_t)row0 * D + ch * 8;
+  if (valid >= 32) {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) *reinterpret_cast<u32x4*>(d0 + (size_t)i * RPI * D) = v[i];
+  } else {
+#pragma unroll
+    for (int i = 0; i < NI; ++i)
+      if (i * RPI + row0 < valid) *reinterpret_cast<u32x4*>(d0 + (size_t)i * RPI * D) = v[i];
+  }
+  // a later write to `stage` must not overtake these reads
+  __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
+}
+
 // Block index -> (query/key block, batch*head).  Workgroups are dispatched
 // round-robin over the 8 XCDs (each with its own L2), so id mod 8 picks the
 // XCD.  Every head's blocks go to one XCD (bh mod 8 = id mod 8), and within an

@@ -445,20 +445,15 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     }
     return;
   }
-  if (qrow < Nq) {
-    uint16_t* Oh = p.O + qhead + (size_t)qrow * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const u32x2 v = pack_bf16x4(oacc[db][qd * 4 + 0] * inv, oacc[db][qd * 4 + 1] * inv,
-                                    oacc[db][qd * 4 + 2] * inv, oacc[db][qd * 4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(Oh + db * 32 + qd * 8 + g * 4) = v;
-      }
-    if (g == 0)
-      p.LSE[(size_t)bc.bh * Nq + qrow] =
-          l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+  // O leaves through the K buffers, which nothing reads after the last
+  // tile's scores (and the barrier before the last P V product): rows
+  // 32 w .. 32 w + 31 of the two K tiles for wavefront w
+  if (q0w < Nq) {
+    char* stage = (wave < 2 ? kbuf0 : kbuf1) + (wave & 1) * 32 * RB;
+    store_rows_staged<D>(stage, oacc, inv, p.O + qhead + (size_t)q0w * D, Nq - q0w, lane);
   }
+  if (qrow < Nq && g == 0)
+    p.LSE[(size_t)bc.bh * Nq + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 // Merge of the split-KV partial results of one row: LSE = log sum_s exp(LSE_s)

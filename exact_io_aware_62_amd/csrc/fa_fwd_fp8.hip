@@ -368,25 +368,23 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(FwdParams p) {
     __syncthreads();
     if (odd) pv_only(P1{}, vbuf1);
     else pv_only(P0{}, vbuf0);
+    // every wavefront is done with the V tile before the epilogue reuses it
+    __syncthreads();
   }
 
   // epilogue: O = O_acc * v_descale / l, LSE of the exact scores
   const float l_tot = sum_xor32(l_run);
   const float inv = l_tot > 0.f ? p.v_descale / l_tot : 0.f;
-  if (qrow < N) {
-    uint16_t* Oh = p.O + (size_t)bc.bh * N * D + (size_t)qrow * D;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-#pragma unroll
-      for (int qd = 0; qd < 4; ++qd) {
-        const u32x2 v = pack_bf16x4(oacc[db][qd * 4 + 0] * inv, oacc[db][qd * 4 + 1] * inv,
-                                    oacc[db][qd * 4 + 2] * inv, oacc[db][qd * 4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(Oh + db * 32 + qd * 8 + g * 4) = v;
-      }
-    if (g == 0)
-      p.LSE[(size_t)bc.bh * N + qrow] =
-          l_tot > 0.f ? (m_run - kOff + __log2f(l_tot)) * kLn2 : -INFINITY;
+  // O (bf16, 32 rows of 2D bytes per wavefront) leaves through one of the
+  // four 8-bit tile buffers (64 rows of D bytes each) per wavefront
+  if (q0w < N) {
+    char* stage = wave == 0 ? kbuf0 : wave == 1 ? kbuf1 : wave == 2 ? vbuf0 : vbuf1;
+    store_rows_staged<D>(stage, oacc, inv, p.O + (size_t)bc.bh * N * D + (size_t)q0w * D, N - q0w,
+                         lane);
   }
+  if (qrow < N && g == 0)
+    p.LSE[(size_t)bc.bh * N + qrow] =
+        l_tot > 0.f ? (m_run - kOff + __log2f(l_tot)) * kLn2 : -INFINITY;
 }
 
 template <int D>

@@ -141,3 +141,74 @@ def test_fp8_transposed_value_reads(d):
                 j = 8 * t + e
                 R = 32 * (t >> 1) + 16 * (t & 1) + 8 * (e >> 2) + 4 * g + (e & 3)
                 assert R == 32 * (j // 16) + 8 * ((j % 16) // 4) + 4 * g + j % 4
+
+
+# --- output staging (store_rows_staged) -------------------------------------
+# A wavefront's 32 output rows go through a 32 x 2D-byte LDS area: lane
+# r + 32 g writes 8 bytes per (column block db, quad qd) at row r, logical
+# chunk db*4 + qd, half g; then lane l reads 16 bytes of row
+# i * RPI + l // CPR, logical chunk l % CPR, and stores them to that row of
+# the output.  Chunks are XOR-swizzled by the row's 256-byte bank line:
+# row & 15 at D = 128, (row >> 1) & 7 at D = 64.
+
+def stage_off(D, row, chunk):
+    cpr = D // 8
+    line = row if D == 128 else row >> 1
+    return row * 2 * D + ((chunk ^ (line & (cpr - 1))) << 4)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_staged_rows_round_trip(D):
+    # every (row, column) written by the accumulator layout is read back by
+    # exactly one lane and lands in the same row and column of the output
+    cpr, rpi = D // 8, 64 // (D // 8)
+    lds = {}
+    for lane in range(64):
+        r, g = lane & 31, lane >> 5
+        for db in range(D // 32):
+            for qd in range(4):
+                a = stage_off(D, r, db * 4 + qd) + g * 8
+                for e in range(4):   # four bf16 values, columns db*32 + qd*8 + g*4 + e
+                    col = db * 32 + qd * 8 + g * 4 + e
+                    key = a + 2 * e
+                    assert key not in lds
+                    assert 0 <= key < 32 * 2 * D
+                    lds[key] = (r, col)
+    assert len(lds) == 32 * D
+    seen = set()
+    for i in range(32 // rpi):
+        for lane in range(64):
+            row, ch = i * rpi + lane // cpr, lane % cpr
+            a = stage_off(D, row, ch)
+            for e in range(8):   # 16 bytes = columns ch*8 .. ch*8+7 of the output row
+                assert lds[a + 2 * e] == (row, ch * 8 + e)
+                seen.add((row, ch * 8 + e))
+    assert len(seen) == 32 * D
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_staged_rows_bank_use(D):
+    # ds_write_b64: each 32-lane half of an instruction (256 bytes) should
+    # touch every bank at most twice; ds_read_b128: each 16-lane quarter
+    # (256 bytes) at most once per 64 banks, i.e. distinct banks
+    cpr, rpi = D // 8, 64 // (D // 8)
+    for db in range(D // 32):
+        for qd in range(4):
+            for lo in (0, 32):
+                count = {}
+                for lane in range(lo, lo + 32):
+                    r, g = lane & 31, lane >> 5
+                    a = stage_off(D, r, db * 4 + qd) + g * 8
+                    for w in range(2):
+                        b = (a // 4 + w) % 64
+                        count[b] = count.get(b, 0) + 1
+                assert max(count.values()) <= 2
+    for i in range(32 // rpi):
+        for lo in range(0, 64, 16):
+            banks = set()
+            for lane in range(lo, lo + 16):
+                row, ch = i * rpi + lane // cpr, lane % cpr
+                a = stage_off(D, row, ch)
+                for w in range(4):
+                    banks.add((a // 4 + w) % 64)
+            assert len(banks) == 64
