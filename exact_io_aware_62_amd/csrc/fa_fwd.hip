@@ -92,12 +92,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const int q0w = qb * BQ + wave * 32;   // first query row of this wavefront
   const int qrow = q0w + r;              // this lane's query row
 
-  // Q fragments (B operand of S^T = K Q^T): row qrow, columns kk*16 + g*8 ..+7
+  // Q fragments (B operand of S^T = K Q^T): row qrow, columns kk*16 + g*8 ..+7,
+  // filled from LDS before the first tile
   bf16x8 qf[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk)
-    qf[kk] = as_bf16x8(qrow < Nq ? ldg16(Qh + (size_t)qrow * D + kk * 16 + g * 8)
-                                 : zero_u32x4());
 
   // key range and tile schedule
   const int kend = CAUSAL ? max(0, min(Nk, (qb + 1) * BQ + dlt)) : Nk;
@@ -405,7 +402,24 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   int tc = next_tile(tbeg);
   int tn = tc < ntiles ? next_tile(tc + 1) : ntiles;
   if (tc < ntiles) {
+    // The workgroup's 128 Q rows come in as whole-row copies (a lane reading
+    // its own row straight from global memory would touch 32 rows per load)
+    // into K buffer 1 (rows 0..63) and V buffer 0 (rows 64..127), both unused
+    // until the first tile's copies; each wavefront then reads its 32 rows
+    // with the conflict-free row read.  The first iteration's barrier orders
+    // these reads before the copies that refill the two buffers.
+    T::template copy<NW>(Qh, qb * BQ, Nq, kbuf1, wave, lofs);
+    if (qb * BQ + 64 < Nq) T::template copy<NW>(Qh, qb * BQ + 64, Nq, vbuf0, wave, lofs);
     load_k(tc, 0);
+    wait_vmem();
+    __syncthreads();
+    {
+      const char* qt = (wave < 2 ? kbuf1 : vbuf0) + (wave & 1) * 32 * RB;
+#pragma unroll
+      for (int kk = 0; kk < NKK; ++kk)
+        qf[kk] = as_bf16x8(qrow < Nq ? *reinterpret_cast<const u32x4*>(qt + (oa.xr ^ (kk << 5)) + oa.ar)
+                                     : zero_u32x4());
+    }
     iteration(P0{}, std::true_type{}, tc, tn);
     // whole pairs of tiles: the loop body has one entry and one exit, which
     // keeps O in one register set across both halves
