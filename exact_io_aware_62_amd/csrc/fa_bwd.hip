@@ -415,44 +415,45 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
 
   const int q0w = qb * BQ + wave * 32;
   const int qrow = q0w + r;
+  // Q, dO (and O for D) fragments: row qrow, columns kk*16 + g*8 .. +7,
+  // filled from LDS before the first tile (see below)
   bf16x8 qf[NKK], of[NKK];
-#pragma unroll
-  for (int kk = 0; kk < NKK; ++kk) {
-    const size_t off = (size_t)qrow * D + kk * 16 + g * 8;
-    qf[kk] = as_bf16x8(qrow < Nq ? ldg16(p.Q + qhead + off) : zero_u32x4());
-    of[kk] = as_bf16x8(qrow < Nq ? ldg16(p.dO + qhead + off) : zero_u32x4());
-  }
   const float lse2 = qrow < Nq ? lse_to_log2(p.LSE[(size_t)bc.bh * Nq + qrow]) : INFINITY;
-  float dsum;
-  if constexpr (FUSED_D) {
-    // chunk c = 2 kk + g of the row (columns 8c .. 8c+7) is in of[kk]
-    float part[NKK];
+  float dsum = 0.f;
+  const OperandAddr<T> oa = operand_addr<T>(lane);
+  // D for this lane's row from the O rows at `orow` (this wavefront's 32 rows
+  // in the LDS tile format) and of[]
+  auto form_d = [&](const char* orow) FA_INLINE {
+    if constexpr (FUSED_D) {
+      // chunk c = 2 kk + g of the row (columns 8c .. 8c+7) is in of[kk]
+      float part[NKK];
 #pragma unroll
-    for (int kk = 0; kk < NKK; ++kk) {
-      const u32x4 o = qrow < Nq ? ldg16(p.O + qhead + (size_t)qrow * D + kk * 16 + g * 8)
-                                : zero_u32x4();
-      const u32x4 gd = __builtin_bit_cast(u32x4, of[kk]);
-      float acc = 0.f;
+      for (int kk = 0; kk < NKK; ++kk) {
+        const u32x4 o = qrow < Nq ? *reinterpret_cast<const u32x4*>(orow + (oa.xr ^ (kk << 5)) + oa.ar)
+                                  : zero_u32x4();
+        const u32x4 gd = __builtin_bit_cast(u32x4, of[kk]);
+        float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        acc = __builtin_fmaf(__uint_as_float(o[i] << 16), __uint_as_float(gd[i] << 16), acc);
-        acc = __builtin_fmaf(__uint_as_float(o[i] & 0xffff0000u),
-                             __uint_as_float(gd[i] & 0xffff0000u), acc);
+        for (int i = 0; i < 4; ++i) {
+          acc = __builtin_fmaf(__uint_as_float(o[i] << 16), __uint_as_float(gd[i] << 16), acc);
+          acc = __builtin_fmaf(__uint_as_float(o[i] & 0xffff0000u),
+                               __uint_as_float(gd[i] & 0xffff0000u), acc);
+        }
+        part[kk] = acc;
       }
-      part[kk] = acc;
+      // tree over chunk bits D/16 .. 2 inside the lane (kk bits NKK/2 .. 1),
+      // then chunk bit 1 (= g) across the two lane halves
+#pragma unroll
+      for (int off = NKK / 2; off > 0; off >>= 1)
+#pragma unroll
+        for (int kk = 0; kk < NKK; ++kk)
+          if (!(kk & off)) part[kk] = part[kk] + part[kk | off];
+      dsum = sum_xor32(part[0]);
+      if (g == 0 && qrow < Nq) p.Dsum[(size_t)bc.bh * Nq + qrow] = dsum;
+    } else {
+      dsum = qrow < Nq ? p.Dsum[(size_t)bc.bh * Nq + qrow] : 0.f;
     }
-    // tree over chunk bits D/16 .. 2 inside the lane (kk bits NKK/2 .. 1),
-    // then chunk bit 1 (= g) across the two lane halves
-#pragma unroll
-    for (int off = NKK / 2; off > 0; off >>= 1)
-#pragma unroll
-      for (int kk = 0; kk < NKK; ++kk)
-        if (!(kk & off)) part[kk] = part[kk] + part[kk | off];
-    dsum = sum_xor32(part[0]);
-    if (g == 0 && qrow < Nq) p.Dsum[(size_t)bc.bh * Nq + qrow] = dsum;
-  } else {
-    dsum = qrow < Nq ? p.Dsum[(size_t)bc.bh * Nq + qrow] : 0.f;
-  }
+  };
 
   const int kend = CAUSAL ? max(0, min(Nk, (qb + 1) * BQ + dlt)) : Nk;
   const int ntiles = (kend + BK - 1) / BK;
@@ -484,7 +485,6 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     copy_async<T, NW>(Vh, t * BK, Nk, lds_addr(vbuf) + stage * T::kBytes, wave, lofs);
   };
 
-  const OperandAddr<T> oa = operand_addr<T>(lane);
   constexpr int NS = 4 * NKK + 4 * NDB;   // products per tile
   constexpr int PF = 3;                   // operand reads issued this many products ahead
   // operand of product j (see the schedule above)
@@ -581,9 +581,46 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     });
   };
 
-  int t = next_tile(0);
+  // The rows of the workgroup's query block arrive as whole-row copies into
+  // LDS (a lane loading its own row would touch 32 rows per load), in two
+  // phases that each fill both stages of the two tile buffers:
+  //   1. dO -> K buffers, O -> V buffers; read of[] and form D;
+  //   2. Q -> stage 1 of both buffers while the first key tile goes to
+  //      stage 0; read qf[].  The first iteration's barrier orders these
+  //      reads before the copy that refills stage 1.
+  // Rows 32 w .. 32 w + 31 of the block sit in stage w / 2, rows
+  // 32 (w % 2) .. of that stage.
+  const int t_first = next_tile(0);
+  const int r0 = qb * BQ;
+  const bool upper = r0 + 64 < Nq;   // rows 64..127 of the block exist
+  const int wrow = (wave & 1) * 32 * RB;
+  auto copy_block = [&](const uint16_t* src, int dst0, int dst1) FA_INLINE {
+    copy_async<T, NW>(src, r0, Nq, dst0, wave, lofs);
+    if (upper) copy_async<T, NW>(src, r0 + 64, Nq, dst1, wave, lofs);
+  };
+  auto read_rows = [&](const char* rows, bf16x8 (&f)[NKK]) FA_INLINE {
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk)
+      f[kk] = as_bf16x8(qrow < Nq ? *reinterpret_cast<const u32x4*>(rows + (oa.xr ^ (kk << 5)) + oa.ar)
+                                  : zero_u32x4());
+  };
+  copy_block(p.dO + qhead, lds_addr(kbuf), lds_addr(kbuf) + T::kBytes);
+  if constexpr (FUSED_D) copy_block(p.O + qhead, lds_addr(vbuf), lds_addr(vbuf) + T::kBytes);
+  wait_vmem();
+  __syncthreads();
+  read_rows(kbuf + (wave >> 1) * T::kBytes + wrow, of);
+  form_d(vbuf + (wave >> 1) * T::kBytes + wrow);
+  if (t_first < ntiles) {
+    __syncthreads();   // every wavefront has read its dO and O rows
+    copy_async<T, NW>(p.Q + qhead, r0, Nq, lds_addr(kbuf) + T::kBytes, wave, lofs);
+    if (upper) copy_async<T, NW>(p.Q + qhead, r0 + 64, Nq, lds_addr(vbuf) + T::kBytes, wave, lofs);
+    issue(t_first, 0);
+    wait_vmem();
+    __syncthreads();
+    read_rows((wave < 2 ? kbuf : vbuf) + T::kBytes + wrow, qf);
+  }
+  int t = t_first;
   int stage = 0;
-  if (t < ntiles) issue(t, 0);
   // one loop body for both stages keeps dQ in one register set
   while (t < ntiles) {
     wait_vmem();
@@ -602,6 +639,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   // tile (w = 2, 3) serve wavefront w.  Block-sparse grids store straight
   // from the accumulator layout, which measured faster there.
   if constexpr (!SPARSE) {
+    // with no key tile there was no loop barrier after the dO and O reads
+    if (t_first >= ntiles) __syncthreads();
     if (q0w < Nq) {
       char* st = (wave < 2 ? kbuf : vbuf) + stage * T::kBytes + (wave & 1) * 32 * RB;
       store_rows_staged<D>(st, dq, p.scale, p.dQ + qhead + (size_t)q0w * D, Nq - q0w, lane);
