@@ -26,6 +26,8 @@ CASES = [
     (2, 2, 1, 2048, 128, "causal"),        # one decoding step over a long cache
     (1, 3, 7, 300, 64, "causal"),          # a few new tokens
     (2, 2, 100, 37, 64, "causal"),         # more queries than keys: empty leading rows
+    (1, 2, 300, 40, 128, "causal"),        # whole query blocks without a key (no key tile)
+    (1, 2, 200, 60, 64, "causal"),
     (1, 2, 256, 512, 128, "dense"),
     (2, 1, 200, 333, 128, "causal"),
     (1, 2, 130, 260, 64, "blocksparse"),
@@ -90,6 +92,13 @@ def test_no_keys_and_no_queries(fa):
                              dk=torch.full_like(k, 7.0), dv=torch.full_like(k, 7.0))
     torch.cuda.synchronize()
     assert bool((dk == 0).all()) and bool((dv == 0).all())
+    # no keys: dQ = 0 over the queries (the dQ kernel runs no key tile)
+    for causal in (False, True):
+        do = torch.randn_like(q)
+        dq, dk, dv = fa.backward(q, empty, empty, o, do, lse, 0.125, causal,
+                                 dq=torch.full_like(q, 7.0))
+        torch.cuda.synchronize()
+        assert bool((dq == 0).all())
 
 
 def test_suffix_of_square_causal_on_gpu(fa):
