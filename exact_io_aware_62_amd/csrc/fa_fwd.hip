@@ -263,6 +263,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     constexpr int NJ = 4 * NDB, PF = 2, J0 = 2;   // exps in products J0 .. NJ-1
     bf16x8 vfr[NJ];
     __builtin_amdgcn_sched_barrier(0);
+    // Issue priority 1 while the softmax runs under the products: of the two
+    // wavefronts sharing a SIMD, the one interleaving vector work with its
+    // P V products goes first, and the other one's score products (phase A,
+    // matrix work only) fill the matrix core around it.  Measured 2-3%
+    // faster than equal priority; raising phase A instead measured slower.
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int j = 0; j < PF; ++j) vfr[j] = vread(vt, j);
     float a0 = 0.f, a1 = 0.f;
@@ -309,6 +315,8 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    __builtin_amdgcn_s_setprio(0);
+    __builtin_amdgcn_sched_barrier(0);
     return a0 + a1;
   };
   // O += P V alone (the last product of a wavefront), same issue order
