@@ -180,6 +180,19 @@ def draw_inputs_nqk(B: int, H: int, Nq: int, Nk: int, d: int, seed: int) -> dict
 
 
 
+def draw_inputs_device(B: int, H: int, N: int, d: int, seed: int, device="cuda:0"):
+    """Seeded Q, K, V, dO of shape (B, H, N, d) drawn on the device: N(0, 1) from a
+    torch generator seeded with ``seed``, rounded to bf16 by torch, in the order
+    Q, K, V, dO.  For shapes too large to draw on the host (tensors of several GB);
+    a consumer that needs the bits on the host copies them back."""
+    import torch
+    gen = torch.Generator(device=device).manual_seed(seed)
+    out = {}
+    for name in ("q", "k", "v", "do"):
+        out[name] = torch.randn((B, H, N, d), generator=gen, device=device, dtype=torch.bfloat16)
+    return out
+
+
 # ---------------------------------------------------------------------------
 # FP8 (E4M3) inputs.  A tensor is drawn from N(0, 1) in float32 like the bf16
 # inputs, given one per-tensor factor ``descale`` = max|x| / 448 (float32, so the

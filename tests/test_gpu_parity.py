@@ -254,3 +254,38 @@ def test_identical_value_rows(fa):
     o = from_gpu(out["o"])
     row = synth.bf16_bits_to_f64(bits["v"][:, :, :1, :])
     assert np.abs(o - row).max() <= 1e-2 * np.abs(row).max()
+
+
+# ---------------------------------------------------------------------------
+# a tensor of more than 2^31 elements: flat element offsets overflow int32
+# ---------------------------------------------------------------------------
+
+def test_offsets_past_2_31_elements(fa):
+    """B=1, H=8200, N=2048, d=128, causal: 2.15e9 elements per tensor.  The head
+    that starts past element 2^31, the last head and the first one match the oracle
+    (fp64, the exact bf16 inputs copied back from the device)."""
+    torch = torch_mod()
+    B, H, N, d = 1, 8200, 2048, 128
+    assert B * H * N * d > 2 ** 31
+    scale = float(np.float32(d ** -0.5))
+    x = synth.draw_inputs_device(B, H, N, d, 2031)
+    o, lse = fa.forward(x["q"], x["k"], x["v"], scale, True)
+    dq, dk, dv = fa.backward(x["q"], x["k"], x["v"], o, x["do"], lse, scale, True)
+    torch.cuda.synchronize()
+    first_past = -(-(2 ** 31) // (N * d))
+    allowed = oracle.allowed_mask(N, N, True, None, 128)
+    for h in (0, first_past, H - 1):
+        qq, kk, vv, dd = (from_gpu(x[n][0, h]) for n in ("q", "k", "v", "do"))
+        ro, rl, _ = oracle.head_forward(qq, kk, vv, scale, allowed)
+        rq, rk, rv = oracle.head_backward(qq, kk, vv, dd, scale, allowed)
+        errs = {"o": rel_err(from_gpu(o[0, h]), ro),
+                "lse": lse_err(lse[0, h].cpu().numpy(), rl),
+                "dq": rel_err(from_gpu(dq[0, h]), rq),
+                "dk": rel_err(from_gpu(dk[0, h]), rk),
+                "dv": rel_err(from_gpu(dv[0, h]), rv)}
+        print(f"past-2^31 head {h}: " + " ".join(f"{k}={e:.2e}" for k, e in errs.items()),
+              flush=True)
+        for name, e in errs.items():
+            assert e <= (TOL_LSE if name == "lse" else TOL_REL), (h, name, e)
+    del x, o, lse, dq, dk, dv
+    torch.cuda.empty_cache()
