@@ -222,8 +222,8 @@ int fa_fwd_splitkv(const void* Q, const void* K, const void* V,
                    void* O, float* LSE, hipStream_t stream);
 
 /* The split count fa_fwd_splitkv uses for num_splits <= 0 (at least 1): about
- * 2048 workgroups in flight with at least four 64-key tiles per range; 0 for
- * invalid shapes. */
+ * one workgroup per compute unit (256 in flight) with 4 to 256 64-key tiles
+ * per range; 0 for invalid shapes. */
 int fa_fwd_splitkv_num_splits(int B, int H, int Nq, int Nk, int d);
 
 /* Workspace bytes fa_fwd_splitkv needs for that num_splits (0: no split, or

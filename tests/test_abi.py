@@ -219,8 +219,10 @@ def test_nqk_entry_points_validate(lib):
 def test_splitkv_sizing_and_validation(lib):
     # decoding: one query row per head, long cache -> many splits, >= 4 tiles each
     s = lib.fa_fwd_splitkv_num_splits(8, 16, 1, 16384, 128)
-    assert s == 16      # 2048 workgroups / 128 heads, 256 tiles -> 16 tiles per range
-    assert lib.fa_fwd_splitkv_workspace_bytes(8, 16, 1, 16384, 128, 0) == 16 * 128 * 129 * 4
+    assert s == 2       # 256 workgroups (one per CU) / 128 heads
+    assert lib.fa_fwd_splitkv_workspace_bytes(8, 16, 1, 16384, 128, 0) == 2 * 128 * 129 * 4
+    assert lib.fa_fwd_splitkv_num_splits(1, 16, 1, 65536, 128) == 16   # 256 / 16 heads
+    assert lib.fa_fwd_splitkv_num_splits(8, 16, 1, 65536, 128) == 4    # at most 256 tiles each
     # short caches: at least four tiles per range
     assert lib.fa_fwd_splitkv_num_splits(1, 1, 1, 512, 64) == 2
     # a full training shape needs no split
