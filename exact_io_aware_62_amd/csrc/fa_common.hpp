@@ -224,8 +224,10 @@ struct LaneOffsets {
 // The copy from HBM uses global_load_lds_dwordx4: each wavefront instruction
 // writes 64 x 16 contiguous bytes of LDS, lane l at byte 16*l, so lane l
 // fetches whichever logical chunk lives at that physical position.  Rows at
-// or past `n_valid` are fetched from row n_valid - 1 instead (valid memory,
-// finite values); every kernel masks those rows, so they never contribute.
+// or past `n_valid` lie beyond the buffer resource's size, so the hardware
+// range check returns zeros for them: finite values, which matters because a
+// masked probability of 0 times such a row must stay 0 in the P V product
+// (0 * inf or 0 * NaN would not).
 // ---------------------------------------------------------------------------
 // D = 32 serves rows of 64 one-byte values (the FP8 kernel at head dim 64):
 // only the byte size of a row matters to the layout.

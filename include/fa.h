@@ -104,12 +104,16 @@ size_t fa_bwd_workspace_bytes(int B, int H, int N, int d);
 /*
  * Backward pass: gradients of L = sum(dO * O) with respect to Q, K and V,
  * recomputing S and P from Q, K and the saved LSE (digest section "核心方法",
- * Backward recomputation).  Three stream-ordered launches:
- *   1. D_i = sum_k dO_ik * O_ik  (into the workspace);
+ * Backward recomputation).  Two stream-ordered launches:
+ *   1. per block of queries: D_i = sum_k dO_ik * O_ik for the block's rows,
+ *      stored in the workspace, then dQ = scale * dS K with dP = dO V^T and
+ *      dS = P * (dP - D) recomputed tile by tile; dQ is written once, so no
+ *      atomics are needed;
  *   2. per block of keys: dV = P^T dO, dP = dO V^T, dS = P * (dP - D),
- *      dK = scale * dS^T Q;
- *   3. per block of queries: dQ = scale * dS K, recomputing dS; dQ is
- *      written once, so no atomics are needed.
+ *      dK = scale * dS^T Q, reading D from the workspace.
+ * fa_bwd_dq_dsum followed by fa_bwd_dkdv (below) are exactly these two
+ * launches; the three-stage order fa_bwd_dsum, fa_bwd_dkdv, fa_bwd_dq gives
+ * the same bits.
  *
  *   Q, K, V, O, dO   [B, H, N, d] bf16, read only.  O and LSE must be the
  *                    outputs of fa_fwd for the same Q, K, V, scale and

@@ -43,6 +43,42 @@ def test_keep_mask_bitwise(fa, B, H, N, p, seed, offset):
         assert np.array_equal(keep.reshape(B * H, N, N)[bh].astype(bool), ref), bh
 
 
+def _p_bracket(w: int):
+    """float32 probabilities p_keep, p_drop whose thresholds floor(p * 2^32) lie just
+    at or below the 32-bit word w and just above it."""
+    two32 = 4294967296.0
+    lo = np.float32(w / two32)
+    while int(np.floor(float(lo) * two32)) > w:
+        lo = np.nextafter(lo, np.float32(0))
+    hi = np.float32((w + 1) / two32)
+    while int(np.floor(float(hi) * two32)) <= w:
+        hi = np.nextafter(hi, np.float32(1))
+    return float(lo), float(hi)
+
+
+def test_keep_bits_follow_published_philox_words(fa):
+    """Query 0, keys 0..3 of head 0 with seed 0 and offset 0 are the four words of
+    Philox4x32-10 on the zero counter under the zero key, whose published values are
+    in tests/golden/philox_kat.json.  For each word w, a threshold just at or below w
+    keeps the element and one just above drops it: the GPU generator is pinned to
+    the published output independently of the oracle (to within the float32
+    spacing of p, a few hundred units of 2^-32)."""
+    import json
+    import os
+    torch = torch_mod()
+    with open(os.path.join(os.path.dirname(__file__), "golden", "philox_kat.json")) as f:
+        vec = json.load(f)["vectors"][0]
+    assert vec["counter"] == ["00000000"] * 4 and vec["key"] == ["00000000"] * 2
+    words = [int(x, 16) for x in vec["output"]]
+    for t, w in enumerate(words):
+        p_keep, p_drop = _p_bracket(w)
+        kept = fa.dropout_keep_mask(1, 1, 4, p_keep, 0, 0).cpu().numpy().reshape(4, 4)
+        dropped = fa.dropout_keep_mask(1, 1, 4, p_drop, 0, 0).cpu().numpy().reshape(4, 4)
+        torch.cuda.synchronize()
+        assert kept[0, t] == 1, (t, hex(w), p_keep)
+        assert dropped[0, t] == 0, (t, hex(w), p_drop)
+
+
 CASES = [
     # B, H, N, d, mask, p
     (1, 2, 128, 64, "dense", 0.5),

@@ -125,6 +125,71 @@ def test_small_whole_tensor(fa, case):
 
 
 # ---------------------------------------------------------------------------
+# B*H a multiple of 32: the launches then take the XCD-grouped workgroup order
+# (four heads at a time per XCD) in every kernel that uses it (dK/dV always;
+# the forward and dQ when not causal).  Every head is compared with the oracle.
+# ---------------------------------------------------------------------------
+
+GROUPED = [
+    # B, H, N, d, mask
+    (2, 16, 384, 128, "dense"),
+    (2, 16, 384, 64, "dense"),
+    (2, 16, 512, 64, "butterfly"),
+    (2, 16, 448, 128, "causal"),
+]
+
+
+@pytest.mark.parametrize("case", GROUPED, ids=[f"B{c[0]}H{c[1]}N{c[2]}d{c[3]}-{c[4]}"
+                                               for c in GROUPED])
+def test_grouped_order_every_head(fa, case):
+    B, H, N, d, kind = case
+    assert (B * H) % 32 == 0
+    seed = 300 + N + d
+    causal, bm = _mask_for(kind, N, 128, np.random.default_rng(seed))
+    bits = synth.draw_inputs(B, H, N, d, seed)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    out = run_gpu(fa, bits, scale, causal, bm, 128)
+    for b in range(B):
+        for h in range(H):
+            check_head(out, bits, b, h, scale, causal, bm, 128, tag=f"grouped {case}")
+
+
+# ---------------------------------------------------------------------------
+# output rounding: bf16 round-to-nearest-even
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_output_rounds_to_nearest_even(fa, d):
+    """Q = 0 makes every score 0, so each of the N = 2 rows averages the two value
+    rows with weights exactly 1/2.  Value row 1 is value row 0 plus one bf16 ulp (in
+    magnitude), so every element of O is exactly the midpoint of two neighbouring bf16
+    numbers.  Round-to-nearest-even gives the neighbour with an even last bit;
+    truncation would give row 0's value and rounding half away from zero row 1's."""
+    torch = torch_mod()
+    rng = np.random.default_rng(4000 + d)
+    x = rng.standard_normal(4 * d).astype(np.float32)
+    x = x[np.abs(x) > 1e-2][:d]
+    assert x.size == d
+    v0 = synth.bf16_round_bits(x)                       # uint16 bit patterns
+    v1 = (v0.astype(np.uint32) + 1).astype(np.uint16)   # one ulp up in magnitude
+    even0 = (v0 & 1) == 0
+    assert even0.any() and (~even0).any()               # both cases present
+    bits = {
+        "q": np.zeros((1, 1, 2, d), np.uint16),
+        "k": synth.draw_inputs(1, 1, 2, d, 11)["k"],
+        "v": np.stack([v0, v1])[None, None],
+    }
+    o, lse = fa.forward(to_gpu(bits["q"]), to_gpu(bits["k"]), to_gpu(bits["v"]),
+                        float(np.float32(d ** -0.5)), False)
+    torch.cuda.synchronize()
+    got = o.view(torch.int16).cpu().numpy().view(np.uint16)[0, 0]
+    want = np.where(even0, v0, v1)
+    for row in range(2):
+        assert np.array_equal(got[row], want), (row, got[row][got[row] != want])
+    assert np.abs(lse.cpu().numpy() - np.log(2.0)).max() <= 1e-6
+
+
+# ---------------------------------------------------------------------------
 # the five workloads at full size, sampled heads compared one by one
 # ---------------------------------------------------------------------------
 

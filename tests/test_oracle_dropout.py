@@ -1,10 +1,14 @@
 """Pins of the dropout oracle (oracle/dropout.py) that do not re-type its formulas.
 
 What pins what:
-* the Philox generator: output statistics (uniform words, balanced bits, no
-  correlation between neighbouring counters, keys and streams), the prefix property
-  of the keep mask, and a scalar re-implementation on Python integers that checks the
-  vectorised uint64 arithmetic (consistency only; the statistics are the pin);
+* the Philox generator: the published known-answer vectors of Philox4x32-10
+  (tests/golden/philox_kat.json: Salmon et al., SC 2011, and the Random123 known-answer
+  file), which planted mistakes in the generator (swapped round multipliers, swapped
+  key increments, the key advanced before round 0, output words reordered) each fail;
+  output statistics (uniform words, balanced bits, no correlation between
+  neighbouring counters, keys and streams); the prefix property of the keep mask; and a
+  scalar re-implementation on Python integers that checks the vectorised uint64
+  arithmetic (consistency only);
 * the dropout semantics: p = 0 reduces to the plain oracle exactly; scalar loops over
   the definition for tiny inputs; central finite differences of the dropout forward
   (mask held fixed) against the analytic backward; the mean over many masks of the
@@ -12,7 +16,9 @@ What pins what:
 * planted mistakes in the backward and the forward each fail one of these.
 """
 
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -39,6 +45,65 @@ def _philox_scalar(c, k):
         b = 0xCD9E8D57 * c[2]
         c = [(b // 2**32) ^ c[1] ^ k[0], b % 2**32, (a // 2**32) ^ c[3] ^ k[1], a % 2**32]
     return c
+
+
+_KAT = os.path.join(os.path.dirname(__file__), "golden", "philox_kat.json")
+
+
+def _kat_vectors():
+    with open(_KAT) as f:
+        data = json.load(f)
+    assert data["generator"] == "philox4x32" and data["rounds"] == 10
+    out = []
+    for vec in data["vectors"]:
+        c = [int(x, 16) for x in vec["counter"]]
+        k = [int(x, 16) for x in vec["key"]]
+        r = [int(x, 16) for x in vec["output"]]
+        out.append((vec["name"], c, k, r))
+    return out
+
+
+def _kat_fails(philox) -> bool:
+    """True if `philox` (same signature as the oracle's) misses any published vector."""
+    for _, c, k, r in _kat_vectors():
+        got = [int(np.asarray(w).reshape(-1)[0]) for w in philox(*c, *k)]
+        if got != r:
+            return True
+    return False
+
+
+def test_philox_matches_published_known_answers():
+    """The oracle's generator reproduces the published Philox4x32-10 known-answer
+    vectors word for word (an external pin: the values are the generator authors')."""
+    for name, c, k, r in _kat_vectors():
+        got = [int(np.asarray(w).reshape(-1)[0]) for w in oracle.philox4x32_10(*c, *k)]
+        assert got == r, (name, [f"{x:08x}" for x in got])
+    assert not _kat_fails(oracle.philox4x32_10)
+
+
+@pytest.mark.parametrize("kind", ["swap_multipliers", "swap_weyl", "key_bumped_first",
+                                  "words_reordered"])
+def test_philox_mutants_fail_known_answers(kind, monkeypatch):
+    """Plausible misreadings of the generator, planted in the oracle, each miss the
+    published vectors."""
+    if kind == "swap_multipliers":
+        monkeypatch.setattr(odrop, "_M0", odrop._M1)
+        monkeypatch.setattr(odrop, "_M1", 0xD2511F53)
+        mutant = odrop.philox4x32_10
+    elif kind == "swap_weyl":
+        monkeypatch.setattr(odrop, "_W0", odrop._W1)
+        monkeypatch.setattr(odrop, "_W1", 0x9E3779B9)
+        mutant = odrop.philox4x32_10
+    elif kind == "key_bumped_first":
+        # the key schedule advanced once before round 0 instead of after it
+        def mutant(c0, c1, c2, c3, k0, k1):
+            return odrop.philox4x32_10(c0, c1, c2, c3, (k0 + 0x9E3779B9) % 2**32,
+                                       (k1 + 0xBB67AE85) % 2**32)
+    else:
+        def mutant(c0, c1, c2, c3, k0, k1):
+            w = odrop.philox4x32_10(c0, c1, c2, c3, k0, k1)
+            return w[1], w[0], w[3], w[2]
+    assert _kat_fails(mutant), kind
 
 
 def test_vectorised_philox_matches_scalar_integers():
