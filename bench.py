@@ -8,7 +8,10 @@ seeded synthetic bf16 N(0,1) tensors already resident in HBM when timing starts.
 
 Timing: HIP events on the stream the kernels run on (torch's current stream,
 which is the stream handed to libfa), one event between every kernel launch,
-so each kernel's average duration is measured live over the timed steps.
+so each kernel's duration is measured live in every timed step; the line reports
+medians over the timed steps (means alongside).  After timing, one more step is
+compared bit for bit with the last timed one (deterministic_rerun), and the GPU
+clock is sampled over one second of further steps.
 
 FLOP accounting (algorithmic, not what the kernels execute):
   forward   4 * B * H * N^2 * d, halved for causal, times the active-block
@@ -94,9 +97,62 @@ def measured_traffic(workload: str, kernel: str, launches_per_step: int = 1):
     return entry.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo), or the platform string."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
+def sample_clock(run, seconds: float, torch, dev):
+    """Median, min and max of the GPU's current graphics clock (MHz) sampled every
+    50 ms from another thread while `run` is launched back to back for `seconds`.
+    None when the clock cannot be read on this system."""
+    import threading
+    try:
+        torch.cuda.clock_rate(dev)
+    except Exception:
+        return None
+    samples, stop = [], threading.Event()
+
+    def poll():
+        while not stop.is_set():
+            try:
+                samples.append(float(torch.cuda.clock_rate(dev)))
+            except Exception:
+                return
+            time.sleep(0.05)
+
+    th = threading.Thread(target=poll, daemon=True)
+    # the sampler starts once the GPU is already busy (a first batch of steps queued)
+    for _ in range(20):
+        run()
+    t_end = time.perf_counter() + seconds
+    th.start()
+    while time.perf_counter() < t_end:
+        for _ in range(20):
+            run()
+        torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    if not samples:
+        return None
+    return {"median": float(np.median(samples)), "min": min(samples), "max": max(samples),
+            "samples": len(samples),
+            "source": (f"torch.cuda.clock_rate (current graphics clock) every 50 ms over "
+                       f"{seconds:.1f} s of back-to-back steps")}
+
+
 def cpu_baseline(cfg, bits, budget_s: float, gpu_out=None):
-    """Time the fp64 oracle (fwd + bwd) head by head on host cores until the
-    budget is spent.  Also returns the parity of the GPU result on those heads."""
+    """Time the fp64 oracle head by head on host cores until the budget is spent:
+    the forward alone and forward + backward, per head.  Also returns the parity of
+    the GPU result on those heads."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
@@ -109,13 +165,16 @@ def cpu_baseline(cfg, bits, budget_s: float, gpu_out=None):
     heads = []
     worst = {}
     t_total = 0.0
+    t_fwd = 0.0
     for bh in range(cfg.B * cfg.H):
         b, h = divmod(bh, cfg.H)
         q, k, v, do = (synth.bf16_bits_to_f64(bits[x][b, h]) for x in ("q", "k", "v", "do"))
         t0 = time.perf_counter()
         o, lse, _ = oracle.head_forward(q, k, v, cfg.scale, allowed)
+        t1 = time.perf_counter()
         dq, dk, dv = oracle.head_backward(q, k, v, do, cfg.scale, allowed)
         t_total += time.perf_counter() - t0
+        t_fwd += t1 - t0
         heads.append(bh)
         if gpu_out is not None:
             for name, ref in (("o", o), ("dq", dq), ("dk", dk), ("dv", dv)):
@@ -128,13 +187,22 @@ def cpu_baseline(cfg, bits, budget_s: float, gpu_out=None):
             break
     flops_head = 3.5 * 4.0 * N * N * cfg.d * mask_fraction(cfg)
     tflops = flops_head * len(heads) / t_total / 1e12
+    n_all = cfg.B * cfg.H
     cpu = {
         "value": tflops,
         "unit": "TFLOP/s",
         "cores": int(cores),
         "kind": "oracle",
-        "sample": (f"{len(heads)} of {cfg.B * cfg.H} heads of the same workload, forward + "
+        "sample": (f"{len(heads)} of {n_all} heads of the same workload, forward + "
                    f"backward, fp64 numpy (S and P materialised), {t_total:.1f} s"),
+        "cpu_model": cpu_model(),
+        "fwd_s": t_fwd,
+        "fwd_bwd_s": t_total,
+        "heads_timed": len(heads),
+        "fwd_tflops": 4.0 * N * N * cfg.d * mask_fraction(cfg) * len(heads) / t_fwd / 1e12,
+        # whole workload: measured when every head was timed, else scaled by heads
+        "fwd_s_whole_workload": t_fwd * n_all / len(heads),
+        "fwd_bwd_s_whole_workload": t_total * n_all / len(heads),
     }
     return cpu, worst
 
@@ -255,6 +323,8 @@ def main():
     ap.add_argument("--fp8", action="store_true",
                     help="instead of the training step, time the FP8 forward (fa_fwd_fp8) on "
                          "the workload's shape, next to the bf16 forward")
+    ap.add_argument("--no-clock", dest="clock", action="store_false",
+                    help="skip sampling the GPU clock over 1 s of extra steps")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the oracle timed on host cores (0 disables it)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -357,9 +427,24 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_total = start.elapsed_time(end)
-    ms_per_step = ms_total / args.steps
-    kern_ms = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
+    ms_mean = ms_total / args.steps
+    # medians over the timed steps: per step (first to last event of the step) and per
+    # kernel (the events on either side of its launch)
+    step_ms = [e[0].elapsed_time(e[-1]) for e in evs]
+    ms_per_step = float(np.median(step_ms))
+    kern_ms = {name: float(np.median([e[j].elapsed_time(e[j + 1]) for e in evs]))
                for j, name in enumerate(kernels)}
+    kern_ms_mean = {name: float(np.mean([e[j].elapsed_time(e[j + 1]) for e in evs]))
+                    for j, name in enumerate(kernels)}
+
+    # determinism: one more step into fresh outputs must give the same bits
+    torch.cuda.synchronize()
+    saved = [t.clone() for t in (o, lse, dq, dk, dv)]
+    step()
+    torch.cuda.synchronize()
+    deterministic = all(torch.equal(a, b) for a, b in zip(saved, (o, lse, dq, dk, dv)))
+    del saved
+    clock = sample_clock(step, 1.0, torch, dev) if args.clock else None
 
     frac = mask_fraction(cfg)
     fwd_flops = 4.0 * B * H * N * N * d * frac
@@ -390,8 +475,9 @@ def main():
     bwd_ms = kern_ms["bwd"] if pdrop > 0 else kern_ms["dq"] + kern_ms["dkdv"]
     bwd_tflops = 2.5 * fwd_flops / (bwd_ms * 1e-3) / 1e12
     log(f"[bench] {cfg.name} B{B} H{H} N{N} d{d} causal={causal}: {ms_per_step:.3f} ms/step "
-        f"(wall {wall / args.steps * 1e3:.3f}), fwd+bwd {value:.1f} TFLOP/s, fwd {fwd_tflops:.1f}, "
-        f"bwd {bwd_tflops:.1f}; kernels {json.dumps(kern_ms)}")
+        f"median (mean {ms_mean:.3f}, wall {wall / args.steps * 1e3:.3f}), fwd+bwd "
+        f"{value:.1f} TFLOP/s, fwd {fwd_tflops:.1f}, bwd {bwd_tflops:.1f}; kernel medians "
+        f"{json.dumps(kern_ms)}; deterministic re-run: {deterministic}; clock {clock}")
 
     # keep the last step's outputs for the spot parity check
     torch.cuda.synchronize()
@@ -418,6 +504,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_mean": ms_mean,
+        "timing": "median over the timed steps (HIP events on the launch stream)",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -435,9 +523,12 @@ def main():
         "fwd_frac_of_peak": fwd_tflops / PEAK_BF16_TFLOPS,
         "bwd_tflops": bwd_tflops,
         "kernels": per_kernel,
+        "kernel_ms_mean": kern_ms_mean,
         "roofline": roofline,
         "cpu_baseline": cpu,
         "parity_vs_oracle": parity,
+        "deterministic_rerun": deterministic,
+        "clock_mhz": clock,
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "compute_units": props.multi_processor_count},
         "kernel_source_hash": kernel_source_hash(),
