@@ -29,6 +29,8 @@ FA_ERR_SHAPE = 2
 FA_ERR_UNSUPPORTED = 3
 FA_ERR_WORKSPACE = 4
 FA_ERR_HIP = 5
+FA_ERR_SCRATCH = 6
+NOALLOC_MAX_ROWS = 4194304   # FA_NOALLOC_MAX_ROWS: B*H*N limit of fa_bwd_noalloc
 
 _lib = None
 
@@ -39,6 +41,8 @@ _SIGNATURES = {
     "fa_bwd_workspace_bytes": (_sz, [_i, _i, _i, _i]),
     "fa_bwd": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i,
                     _vp, _vp, _vp, _vp, _sz, _vp]),
+    "fa_bwd_noalloc": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i,
+                            _vp, _vp, _vp, _vp]),
     "fa_bwd_dsum": (_i, [_vp, _vp, _i, _i, _i, _i, _vp, _vp]),
     "fa_bwd_dkdv": (_i, [_vp, _vp, _vp, _vp, _vp, _vp, _i, _i, _i, _i, _f, _i, _vp, _i,
                          _vp, _vp, _vp]),
@@ -258,6 +262,38 @@ def backward(q, k, v, o, do, lse, scale: float | None = None, causal: bool = Fal
     rc = load_library().fa_bwd(*ptrs, *grads, *ws)
     if rc != FA_OK:
         raise LibfaError(rc, "fa_bwd")
+    return tuple(outs)
+
+
+def backward_noalloc(q, k, v, o, do, lse, scale: float | None = None, causal: bool = False,
+                     blockmask=None, mask_block: int = 128, dq=None, dk=None, dv=None):
+    """fa_bwd_noalloc: the gradients of fa_bwd with D kept in the library's static
+    scratch instead of a workspace (B*H*N <= NOALLOC_MAX_ROWS).  Pass dq, dk, dv to
+    allocate nothing here either."""
+    torch = _torch()
+    _check(q, "q", torch.bfloat16)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, N, d]")
+    B, H, N, d = q.shape
+    dev = q.device
+    for name, t in (("k", k), ("v", v), ("o", o), ("do", do)):
+        _check(t, name, torch.bfloat16, q.shape, dev)
+    _check(lse, "lse", torch.float32, (B, H, N), dev)
+    scale = default_scale(d) if scale is None else float(scale)
+    outs = []
+    for name, t in (("dq", dq), ("dk", dk), ("dv", dv)):
+        if t is None:
+            t = torch.empty(q.shape, dtype=torch.bfloat16, device=dev)
+        else:
+            _check(t, name, torch.bfloat16, q.shape, dev)
+        outs.append(t)
+    bm_ptr, mb = _mask_args(blockmask, N, mask_block, dev)
+    rc = load_library().fa_bwd_noalloc(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                       do.data_ptr(), lse.data_ptr(), B, H, N, d, scale,
+                                       int(bool(causal)), bm_ptr, mb, outs[0].data_ptr(),
+                                       outs[1].data_ptr(), outs[2].data_ptr(), _stream_ptr(dev))
+    if rc != FA_OK:
+        raise LibfaError(rc, "fa_bwd_noalloc")
     return tuple(outs)
 
 

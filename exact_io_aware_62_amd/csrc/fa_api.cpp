@@ -201,7 +201,7 @@ int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const v
              const float* LSE, int B, int H, int Nq, int Nk, int d, float scale, int causal,
              const uint8_t* blockmask, int mask_block, float p_drop, uint64_t seed,
              uint32_t offset, void* dQ, void* dK, void* dV, void* workspace,
-             size_t workspace_bytes, hipStream_t stream);
+             size_t workspace_bytes, hipStream_t stream, bool noalloc = false);
 
 }  // namespace
 
@@ -217,6 +217,9 @@ const char* fa_strerror(int status) {
              "mask_block a multiple of 128, 16-byte aligned tensors, sizes below 2^31)";
     case FA_ERR_WORKSPACE: return "libfa: workspace missing or too small";
     case FA_ERR_HIP: return "libfa: HIP runtime error at kernel launch";
+    case FA_ERR_SCRATCH:
+      return "libfa: fa_bwd_noalloc supports at most FA_NOALLOC_MAX_ROWS (4194304) query rows "
+             "B*H*N in its static scratch";
     default: return "libfa: unknown status";
   }
 }
@@ -378,6 +381,14 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O, const voi
                   0, 0, dQ, dK, dV, workspace, workspace_bytes, stream);
 }
 
+int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O, const void* dO,
+                   const float* LSE, int B, int H, int N, int d, float scale, int causal,
+                   const uint8_t* blockmask, int mask_block, void* dQ, void* dK, void* dV,
+                   hipStream_t stream) {
+  return bwd_impl(Q, K, V, O, dO, LSE, B, H, N, N, d, scale, causal, blockmask, mask_block, 0.f,
+                  0, 0, dQ, dK, dV, nullptr, 0, stream, true);
+}
+
 int fa_bwd_nqk(const void* Q, const void* K, const void* V, const void* O, const void* dO,
                const float* LSE, int B, int H, int Nq, int Nk, int d, float scale, int causal,
                const uint8_t* blockmask, int mask_block, void* dQ, void* dK, void* dV,
@@ -419,7 +430,7 @@ int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const v
              const float* LSE, int B, int H, int Nq, int Nk, int d, float scale, int causal,
              const uint8_t* blockmask, int mask_block, float p_drop, uint64_t seed,
              uint32_t offset, void* dQ, void* dK, void* dV, void* workspace,
-             size_t workspace_bytes, hipStream_t stream) {
+             size_t workspace_bytes, hipStream_t stream, bool noalloc) {
   bool empty = false;
   int rc = check_common(B, H, Nq, Nk, d, scale, blockmask, mask_block, &empty);
   if (rc != FA_OK) return rc;
@@ -430,10 +441,20 @@ int bwd_impl(const void* Q, const void* K, const void* V, const void* O, const v
   if (empty && no_keys) return FA_OK;
   if (!empty && (!Q || !O || !dO || !LSE || !dQ)) return FA_ERR_NULL;
   if (!no_keys && (!K || !V || !dK || !dV)) return FA_ERR_NULL;
-  if (!empty && (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, Nq, d)))
+  if (noalloc) {
+    // D goes to the library's static scratch instead of a caller workspace
+    if ((long long)B * H * Nq > fa::kNoallocMaxRows) return FA_ERR_SCRATCH;
+  } else if (!empty && (!workspace || workspace_bytes < fa_bwd_workspace_bytes(B, H, Nq, d))) {
     return FA_ERR_WORKSPACE;
+  }
   if (!all_aligned16({Q, K, V, O, dO, dQ, dK, dV}) || !aligned(LSE, 4) || !aligned(workspace, 4))
     return FA_ERR_UNSUPPORTED;
+  if (noalloc) {
+    // the first HIP call: every argument check above has passed
+    float* ws = nullptr;
+    if (fa::noalloc_scratch(&ws) != hipSuccess) return FA_ERR_HIP;
+    workspace = ws;
+  }
   fa::BwdParams p = bwd_params(Q, K, V, O, dO, LSE, static_cast<float*>(workspace), B, H, Nq,
                                Nk, scale, blockmask, mask_block, dQ, dK, dV);
   set_dropout(p, p_drop, seed, offset);

@@ -20,6 +20,8 @@
 // Both main kernels split the sequence over workgroups the way the forward
 // does (FlashAttention-2 wiki, "技术架构与工作原理", item 2).
 
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 #include "fa_common.hpp"
@@ -722,6 +724,42 @@ hipError_t launch_bwd_dq(const BwdParams& p, int d, bool causal, bool sparse, bo
                          bool dropout, hipStream_t stream) {
   if (dropout && !fused_d) return hipErrorInvalidValue;
   return FA_DISPATCH(launch_dq_t, d, causal, sparse, p, fused_d, dropout, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of fa_bwd_noalloc: D_i for up to kNoallocMaxRows query rows.  In
+// host code the name `scratch` denotes a host-side stand-in, not the device
+// array, so host code never passes it to a kernel or a copy: it uses the
+// address hipGetSymbolAddress returns, looked up once per device (with that
+// device current) and kept.  Every fa_bwd_noalloc call on a GPU shares that
+// GPU's array; D is fully written by the dQ launch before the dK/dV launch
+// reads it, so nothing needs clearing, and calls that overlap on one GPU
+// (other streams) race.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) float scratch[kNoallocMaxRows];
+
+hipError_t noalloc_scratch(float** ptr) {
+  constexpr int kMaxDevices = 64;
+  static std::atomic<float*> addr[kMaxDevices];
+  static std::mutex mu;
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  float* a = addr[dev].load(std::memory_order_acquire);
+  if (a == nullptr) {
+    std::lock_guard<std::mutex> lock(mu);
+    a = addr[dev].load(std::memory_order_relaxed);
+    if (a == nullptr) {
+      void* sym = nullptr;
+      e = hipGetSymbolAddress(&sym, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      a = static_cast<float*>(sym);
+      addr[dev].store(a, std::memory_order_release);
+    }
+  }
+  *ptr = a;
+  return hipSuccess;
 }
 
 }  // namespace fa

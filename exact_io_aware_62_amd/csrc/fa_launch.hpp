@@ -76,4 +76,12 @@ hipError_t launch_bwd_dkdv(const BwdParams& p, int d, bool causal, bool sparse, 
 hipError_t launch_bwd_dq(const BwdParams& p, int d, bool causal, bool sparse, bool fused_d,
                          bool dropout, hipStream_t stream);
 
+// Allocation-free backward: D lives in a static device array of
+// kNoallocMaxRows floats (one per query row, 16 MiB) that every GPU the
+// library runs on holds until the process ends.  noalloc_scratch() returns
+// that array's address on the current device (looked up once per device with
+// hipGetSymbolAddress and cached).
+constexpr long long kNoallocMaxRows = 1LL << 22;
+hipError_t noalloc_scratch(float** ptr);
+
 }  // namespace fa

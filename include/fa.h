@@ -68,7 +68,8 @@ typedef enum {
   FA_ERR_SHAPE = 2,       /* a negative dimension                               */
   FA_ERR_UNSUPPORTED = 3, /* outside the supported domain listed above          */
   FA_ERR_WORKSPACE = 4,   /* workspace NULL or smaller than fa_bwd_workspace_bytes */
-  FA_ERR_HIP = 5          /* the HIP runtime reported an error at launch        */
+  FA_ERR_HIP = 5,         /* the HIP runtime reported an error at launch        */
+  FA_ERR_SCRATCH = 6      /* fa_bwd_noalloc: B*H*N above FA_NOALLOC_MAX_ROWS     */
 } fa_status;
 
 /*
@@ -132,6 +133,32 @@ int fa_bwd(const void* Q, const void* K, const void* V, const void* O,
            const uint8_t* blockmask, int mask_block,
            void* dQ, void* dK, void* dV,
            void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * fa_bwd without a workspace argument, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation.  The call itself allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine); D lives in a static
+ * device array of FA_NOALLOC_MAX_ROWS floats (16 MiB) inside the library,
+ * which every GPU the library runs on holds until the process ends.  Same
+ * kernels and launch order as fa_bwd, so the results are the same bits.
+ *
+ *   Arguments as fa_bwd, minus workspace and workspace_bytes.
+ *   B * H * N must not exceed FA_NOALLOC_MAX_ROWS, else FA_ERR_SCRATCH is
+ *   returned and nothing is launched.
+ *
+ * All calls on one GPU share that GPU's scratch array, which keeps the last
+ * call's D: calls that overlap on one GPU (issued on different streams
+ * without ordering between them) race and give undefined results.  The first
+ * call on a device looks up the array's address there (FA_ERR_HIP if that
+ * fails).  Other errors as fa_bwd.
+ */
+#define FA_NOALLOC_MAX_ROWS 4194304
+int fa_bwd_noalloc(const void* Q, const void* K, const void* V, const void* O,
+                   const void* dO, const float* LSE,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const uint8_t* blockmask, int mask_block,
+                   void* dQ, void* dK, void* dV, hipStream_t stream);
 
 /*
  * The three stages of fa_bwd as separate calls, for callers that schedule

@@ -28,13 +28,13 @@ def test_exports_every_declared_symbol(lib):
                           "fa_fwd_dropout", "fa_bwd_dropout", "fa_dropout_keep_mask",
                           "fa_fwd_nqk", "fa_bwd_nqk", "fa_fwd_splitkv",
                           "fa_fwd_splitkv_num_splits", "fa_fwd_splitkv_workspace_bytes",
-                          "fa_fwd_fp8"}
+                          "fa_fwd_fp8", "fa_bwd_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
 
 
 def test_strerror(lib):
-    for code in range(6):
+    for code in range(7):
         s = fa.strerror(code)
         assert s and isinstance(s, str)
     assert "unknown" in fa.strerror(99)
@@ -268,3 +268,29 @@ def test_fp8_validation(lib):
     assert fwd8(lib, v=FAKE + 8) == fa.FA_ERR_UNSUPPORTED
     assert fwd8(lib, lse=FAKE + 2) == fa.FA_ERR_UNSUPPORTED
     assert fwd8(lib, N=0, q=None, k=None, v=None, o=None, lse=None) == fa.FA_OK
+
+
+def noalloc(lib, q=FAKE, k=FAKE, v=FAKE, o=FAKE, do=FAKE, lse=FAKE, B=1, H=1, N=128, d=64,
+            scale=0.125, causal=0, bm=None, mb=0, dq=FAKE, dk=FAKE, dv=FAKE):
+    return lib.fa_bwd_noalloc(q, k, v, o, do, lse, B, H, N, d, scale, causal, bm, mb, dq, dk,
+                              dv, None)
+
+
+def test_noalloc_entry_point_validates(lib):
+    """fa_bwd_noalloc checks its arguments like fa_bwd, and rejects problems whose D
+    would not fit its static scratch, all before its first HIP call (the scratch
+    address lookup)."""
+    assert fa.NOALLOC_MAX_ROWS == 1 << 22
+    assert noalloc(lib, B=-1) == fa.FA_ERR_SHAPE
+    assert noalloc(lib, d=96) == fa.FA_ERR_UNSUPPORTED
+    assert noalloc(lib, scale=0.0) == fa.FA_ERR_UNSUPPORTED
+    assert noalloc(lib, dq=None) == fa.FA_ERR_NULL
+    assert noalloc(lib, q=FAKE + 2) == fa.FA_ERR_UNSUPPORTED
+    assert noalloc(lib, bm=FAKE, mb=64) == fa.FA_ERR_UNSUPPORTED
+    # one row past the limit, and far past it
+    assert noalloc(lib, B=1, H=1, N=(1 << 22) + 1) == fa.FA_ERR_SCRATCH
+    assert noalloc(lib, B=64, H=16, N=8192) == fa.FA_ERR_SCRATCH
+    assert "FA_NOALLOC_MAX_ROWS" in fa.strerror(fa.FA_ERR_SCRATCH)
+    # an empty problem launches nothing
+    assert noalloc(lib, N=0, q=None, k=None, v=None, o=None, do=None, lse=None, dq=None,
+                   dk=None, dv=None) == fa.FA_OK
