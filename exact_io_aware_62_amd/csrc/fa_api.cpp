@@ -88,6 +88,7 @@ fa::BwdParams bwd_params(const void* Q, const void* K, const void* V, const void
   p.scale_log2 = scale * kLog2e;
   p.drop_thresh = 0;
   p.drop_scale = 1.f;
+  p.drop_keep = 1.f;
   p.seed_lo = p.seed_hi = p.drop_offset = 0;
   return p;
 }
@@ -109,12 +110,17 @@ int check_dropout(float p_drop) {
 }
 
 // The kernels' dropout fields: drop iff the Philox word < floor(p * 2^32);
-// kept values are multiplied by 1 / (1 - p) (fp32).
+// kept values are multiplied by 1 / (1 - p) (fp32), which the kernels apply
+// once to their accumulated outputs.
+void set_dropout_keep(fa::FwdParams&, float) {}
+void set_dropout_keep(fa::BwdParams& p, float p_drop) { p.drop_keep = 1.0f - p_drop; }
+
 template <class Params>
 void set_dropout(Params& p, float p_drop, uint64_t seed, uint32_t offset) {
   const double t = std::floor((double)p_drop * 4294967296.0);
   p.drop_thresh = t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
   p.drop_scale = 1.0f / (1.0f - p_drop);
+  set_dropout_keep(p, p_drop);
   p.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);
   p.seed_hi = (uint32_t)(seed >> 32);
   p.drop_offset = offset;

@@ -74,7 +74,10 @@ __global__ __launch_bounds__(256) void dsum_kernel(BwdParams p, long long rows) 
 //    at most 256 vector registers (two wavefronts per SIMD, no accumulator
 //    registers), and the LDS footprint lets two workgroups share a CU.
 // ---------------------------------------------------------------------------
-//    DROPOUT: dV^T += dO^T (P keep / (1 - p)) and dS = P (dP keep / (1 - p) - D).
+//    DROPOUT: dV^T += dO^T (P keep / (1 - p)) and dS = P (dP keep / (1 - p) - D),
+//    computed as dV = (1 / (1 - p)) (P keep)^T dO and dS = (1 / (1 - p)) P (dP keep -
+//    D (1 - p)): the loop only zeroes dropped elements and takes D times 1 - p,
+//    and the factor 1 / (1 - p) is applied to dV and dK once, at the store.
 //    A lane holds one key and 16 queries, while one Philox draw covers four
 //    consecutive keys of one query; so the four lanes of a quad (keys
 //    4c .. 4c+3) each draw for a different query and exchange the 4-bit
@@ -157,6 +160,8 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
   // loaded before that tile's LDS-DMA copies are issued (vector-memory waits
   // complete in issue order, so waiting for it then does not wait for the
   // copies) and converted and stored only after the current tile's compute.
+  // (Spreading the 2 BQ values over all four wavefronts measured 1-1.5%
+  // slower: every wavefront then waits for its copies at this point.)
   float rowv = 0.f;
   int rowq = 0;
   const auto lofs = TQ::template lane_offsets<NW>(wave, lane);
@@ -174,7 +179,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
     if (tid < 2 * BQ) {
       float v;
       if (tid < BQ) v = rowq < Nq ? lse_to_log2(rowv) : INFINITY;
-      else v = rowq < Nq ? rowv : 0.f;
+      else v = rowq < Nq ? (DROPOUT ? rowv * p.drop_keep : rowv) : 0.f;
       rowbuf[bufi * 2 * BQ + tid] = v;
     }
   };
@@ -283,7 +288,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
             float t8[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-              t8[e] = ((keepbits >> (i - 7 + e)) & 1u) ? s[i - 7 + e] * p.drop_scale : 0.f;
+              t8[e] = ((keepbits >> (i - 7 + e)) & 1u) ? s[i - 7 + e] : 0.f;
             pb[i >> 3] = pack_bf16x8(t8[0], t8[1], t8[2], t8[3], t8[4], t8[5], t8[6], t8[7]);
           } else {
             pb[i >> 3] = pack_c8(s, i - 7);
@@ -308,7 +313,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
       for (int i = j * 16 / NJ; i < (j + 1) * 16 / NJ; ++i) {
         const float* dq4 = dsum + (i >> 2) * 8 + g * 4;
         float dpv = dp[i];
-        if constexpr (DROPOUT) dpv = ((keepbits >> i) & 1u) ? dpv * p.drop_scale : 0.f;
+        if constexpr (DROPOUT) dpv = ((keepbits >> i) & 1u) ? dpv : 0.f;
         dp[i] = s[i] * (dpv - dq4[i & 3]);
         if ((i & 7) == 7) sb[i >> 3] = pack_c8(dp, i - 7);
       }
@@ -368,8 +373,9 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
   }
   if (kw < Nk) {
     char* stage = kbuf + wave * 32 * RB;
-    store_rows_staged<D>(stage, dv, 1.f, p.dV + khead + (size_t)kw * D, Nk - kw, lane);
-    store_rows_staged<D>(stage, dk, p.scale, p.dK + khead + (size_t)kw * D, Nk - kw, lane);
+    const float ds = DROPOUT ? p.drop_scale : 1.f;
+    store_rows_staged<D>(stage, dv, ds, p.dV + khead + (size_t)kw * D, Nk - kw, lane);
+    store_rows_staged<D>(stage, dk, p.scale * ds, p.dK + khead + (size_t)kw * D, Nk - kw, lane);
   }
 }
 
@@ -397,7 +403,9 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
 //    the same to the bit; the dK/dV kernel then reads it.
 // ---------------------------------------------------------------------------
 //    DROPOUT: dS = P (dP keep / (1 - p) - D), with the keep bits of the tile
-//    drawn (as in the forward) while its scores are on the matrix cores.
+//    drawn (as in the forward) while its scores are on the matrix cores; the
+//    loop forms P (dP keep - D (1 - p)) and the factor 1 / (1 - p) joins the
+//    scale of dQ at the store.
 template <int D, bool CAUSAL, bool SPARSE, bool FUSED_D, bool DROPOUT>
 __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   constexpr int BQ = 128, BK = 64, NW = 4;
@@ -507,6 +515,9 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     return bf16x8_from_halves(lds_tr_b64(rk + oa.at0), lds_tr_b64(rk + oa.at1));
   };
 
+  // D as the loop uses it: times 1 - p with dropout (see the kernel comment);
+  // set once D is known, after the rows are read below
+  float dsum_k = 0.f;
   auto compute = [&](int stage, int t) FA_INLINE {
     const char* kt = kbuf + stage * T::kBytes;
     const char* vt = vbuf + stage * T::kBytes;
@@ -572,8 +583,8 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
             } else {
               float dpv = dp[kb][i];
               if constexpr (DROPOUT)
-                dpv = ((keepbits >> (kb * 16 + i)) & 1u) ? dpv * p.drop_scale : 0.f;
-              float dsv = s[kb][i] * (dpv - dsum);
+                dpv = ((keepbits >> (kb * 16 + i)) & 1u) ? dpv : 0.f;
+              float dsv = s[kb][i] * (dpv - dsum_k);
               pin(dsv);
               dp[kb][i] = dsv;
               if constexpr ((i & 7) == 7) {
@@ -617,6 +628,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   __syncthreads();
   read_rows(kbuf + (wave >> 1) * T::kBytes + wrow, of);
   form_d(vbuf + (wave >> 1) * T::kBytes + wrow);
+  dsum_k = DROPOUT ? dsum * p.drop_keep : dsum;
   if (t_first < ntiles) {
     __syncthreads();   // every wavefront has read its dO and O rows
     copy_async<T, NW>(p.Q + qhead, r0, Nq, lds_addr(kbuf) + T::kBytes, wave, lofs);
@@ -650,11 +662,12 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     if (t_first >= ntiles) __syncthreads();
     if (q0w < Nq) {
       char* st = (wave < 2 ? kbuf : vbuf) + stage * T::kBytes + (wave & 1) * 32 * RB;
-      store_rows_staged<D>(st, dq, p.scale, p.dQ + qhead + (size_t)q0w * D, Nq - q0w, lane);
+      store_rows_staged<D>(st, dq, DROPOUT ? p.scale * p.drop_scale : p.scale,
+                           p.dQ + qhead + (size_t)q0w * D, Nq - q0w, lane);
     }
   } else if (qrow < Nq) {
     uint16_t* dQh = p.dQ + qhead + (size_t)qrow * D;
-    const float sc = p.scale;
+    const float sc = DROPOUT ? p.scale * p.drop_scale : p.scale;
 #pragma unroll
     for (int db = 0; db < NDB; ++db)
 #pragma unroll

@@ -47,9 +47,11 @@
 namespace fa {
 
 // DROPOUT: P is multiplied by keep / (1 - p) before the P V product (the row
-// sum, and with it LSE, stays that of the plain softmax).  The keep bits of a
-// tile come from the head's Philox stream (DropoutStream) and are drawn while
-// the tile's scores are on the matrix cores.
+// sum, and with it LSE, stays that of the plain softmax).  Inside the loop the
+// dropped probabilities are only zeroed; the common factor 1 / (1 - p) is
+// applied once, with 1 / l, in the epilogue.  The keep bits of a tile come
+// from the head's Philox stream (DropoutStream) and are drawn while the
+// tile's scores are on the matrix cores.
 // MODE 2 (split-KV): the key tiles of a query block are split into p.nsplit
 // ranges of p.tiles_per_split tiles, one workgroup each; a workgroup writes
 // its normalised partial O (fp32) and partial LSE to p.Opart / p.LSEpart, and
@@ -138,9 +140,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     keepbits = (keepbits & ~(0xFu << (4 * u))) | (bits << (4 * u));
     pin(keepbits);
   };
-  // P as it enters the P V product: kept and rescaled, or 0
+  // P as it enters the P V product: kept, or 0 (1 / (1 - p) comes at the end)
   auto dropped = [&](float pe, int e) FA_INLINE -> float {
-    if constexpr (DROPOUT) return ((keepbits >> e) & 1u) ? pe * p.drop_scale : 0.f;
+    if constexpr (DROPOUT) return ((keepbits >> e) & 1u) ? pe : 0.f;
     return pe;
   };
 
@@ -448,7 +450,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 
   // epilogue: combine the two lane halves' partial sums, divide once
   const float l_tot = sum_xor32(l_run);
-  const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+  const float inv = l_tot > 0.f ? (DROPOUT ? p.drop_scale : 1.0f) / l_tot : 0.f;
   if constexpr (SPLIT) {
     if (qrow < Nq) {
       const size_t prow = ((size_t)split * p.BH + bc.bh) * Nq + qrow;

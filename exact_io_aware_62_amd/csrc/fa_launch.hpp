@@ -28,7 +28,7 @@ struct FwdParams {
   // dropout on P (read only by the dropout kernels): element (i, j) of head bh
   // is kept iff philox4x32_10(j/4, i, bh, drop_offset; seed)[j % 4] >= drop_thresh
   uint32_t drop_thresh;      // floor(p * 2^32)
-  float drop_scale;          // 1 / (1 - p), applied to kept probabilities
+  float drop_scale;          // 1 / (1 - p): the kept probabilities' factor, applied to O at the end
   uint32_t seed_lo, seed_hi, drop_offset;
 };
 
@@ -55,7 +55,8 @@ struct BwdParams {
   // dropout on P (read only by the dropout kernels): element (i, j) of head bh
   // is kept iff philox4x32_10(j/4, i, bh, drop_offset; seed)[j % 4] >= drop_thresh
   uint32_t drop_thresh;      // floor(p * 2^32)
-  float drop_scale;          // 1 / (1 - p), applied to kept probabilities
+  float drop_scale;          // 1 / (1 - p), applied to dV, dK and dQ at the end
+  float drop_keep;           // 1 - p: D is taken times this inside the loops
   uint32_t seed_lo, seed_hi, drop_offset;
 };
 

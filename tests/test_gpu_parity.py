@@ -155,6 +155,40 @@ def test_grouped_order_every_head(fa, case):
 
 
 # ---------------------------------------------------------------------------
+# scores that rise along the keys: the running row maximum moves by more than
+# the kernels' rescale slack every few tiles, so the rarely taken rescale of the
+# accumulated O (and of the row sum) runs many times per row
+# ---------------------------------------------------------------------------
+
+RISING = [
+    # B, H, N, d, causal
+    (1, 2, 704, 128, False),
+    (1, 2, 640, 64, True),
+    (2, 1, 333, 128, True),
+]
+
+
+@pytest.mark.parametrize("case", RISING, ids=[f"B{c[0]}H{c[1]}N{c[2]}d{c[3]}-{'causal' if c[4] else 'dense'}"
+                                              for c in RISING])
+def test_rising_scores_rescale(fa, case):
+    B, H, N, d, causal = case
+    bits = synth.draw_inputs(B, H, N, d, 600 + N)
+    k = synth.bf16_bits_to_f64(bits["k"]).astype(np.float32)
+    growth = (1.0 + np.arange(N, dtype=np.float32) / 48.0)[None, None, :, None]
+    bits["k"] = synth.bf16_round_bits(k * growth)
+    scale = float(np.float32(1.0 / np.sqrt(d)))
+    # the scores of the last keys are far above those of the first ones
+    qf = synth.bf16_bits_to_f64(bits["q"][0, 0])
+    kf = synth.bf16_bits_to_f64(bits["k"][0, 0])
+    s = scale * qf @ kf.T * np.log2(np.e)
+    assert s[:, -64:].max() - s[:, :64].max() > 16
+    out = run_gpu(fa, bits, scale, causal, None, 128)
+    for b in range(B):
+        for h in range(H):
+            check_head(out, bits, b, h, scale, causal, None, 128, tag=f"rising {case}")
+
+
+# ---------------------------------------------------------------------------
 # output rounding: bf16 round-to-nearest-even
 # ---------------------------------------------------------------------------
 
