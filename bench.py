@@ -111,42 +111,62 @@ def cpu_model() -> str:
 
 
 def sample_clock(run, seconds: float, torch, dev):
-    """Median, min and max of the GPU's current graphics clock (MHz) sampled every
-    50 ms from another thread while `run` is launched back to back for `seconds`.
-    None when the clock cannot be read on this system."""
-    import threading
+    """Median, min and max of the GPU's current graphics clock (MHz) while `run` keeps the
+    GPU busy: batches of steps are queued and the clock is read from this same thread
+    while the queued work runs (a sampler thread would hold up the launches and let the
+    GPU idle).  None when the clock cannot be read on this system."""
     try:
         torch.cuda.clock_rate(dev)
     except Exception:
         return None
-    samples, stop = [], threading.Event()
-
-    def poll():
-        while not stop.is_set():
-            try:
-                samples.append(float(torch.cuda.clock_rate(dev)))
-            except Exception:
-                return
-            time.sleep(0.05)
-
-    th = threading.Thread(target=poll, daemon=True)
-    # the sampler starts once the GPU is already busy (a first batch of steps queued)
-    for _ in range(20):
+    samples = []
+    for _ in range(20):           # queue work ahead before the first reading
         run()
     t_end = time.perf_counter() + seconds
-    th.start()
+    batches = 0
     while time.perf_counter() < t_end:
-        for _ in range(20):
+        for _ in range(10):
             run()
-        torch.cuda.synchronize()
-    stop.set()
-    th.join()
+        try:
+            samples.append(float(torch.cuda.clock_rate(dev)))
+        except Exception:
+            break
+        batches += 1
+        if batches % 8 == 0:      # bound the queue depth
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
     if not samples:
         return None
     return {"median": float(np.median(samples)), "min": min(samples), "max": max(samples),
             "samples": len(samples),
-            "source": (f"torch.cuda.clock_rate (current graphics clock) every 50 ms over "
-                       f"{seconds:.1f} s of back-to-back steps")}
+            "source": (f"torch.cuda.clock_rate (current graphics clock) read between queued "
+                       f"steps over {seconds:.1f} s of back-to-back steps")}
+
+
+def gemm_reference(torch, dev, n: int = 8192, reps: int = 10):
+    """TFLOP/s of a plain dense bf16 product (n x n x n, torch.matmul -> hipBLASLt) on the
+    same GPU, median of `reps` timed calls: what a matrix-core-bound library kernel
+    reaches on this machine at the clock it runs at, as context for the attention kernels'
+    own rates (the roofline's peak stays the published one)."""
+    a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
+    c = torch.empty(n, n, device=dev, dtype=torch.bfloat16)
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        torch.matmul(a, b, out=c)
+        e1.record()
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    ms = float(np.median(ts))
+    del a, b, c
+    tf = 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+    return {"tflops": tf, "frac_of_peak": tf / PEAK_BF16_TFLOPS, "ms": ms,
+            "what": f"torch.matmul bf16 {n}x{n}x{n} (hipBLASLt), median of {reps}"}
 
 
 def cpu_baseline(cfg, bits, budget_s: float, gpu_out=None):
@@ -325,6 +345,8 @@ def main():
                          "the workload's shape, next to the bf16 forward")
     ap.add_argument("--no-clock", dest="clock", action="store_false",
                     help="skip sampling the GPU clock over 1 s of extra steps")
+    ap.add_argument("--no-gemm-ref", dest="gemm_ref", action="store_false",
+                    help="skip timing the dense bf16 GEMM reference")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="budget for the oracle timed on host cores (0 disables it)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -445,6 +467,7 @@ def main():
     deterministic = all(torch.equal(a, b) for a, b in zip(saved, (o, lse, dq, dk, dv)))
     del saved
     clock = sample_clock(step, 1.0, torch, dev) if args.clock else None
+    gemm = gemm_reference(torch, dev) if args.gemm_ref else None
 
     frac = mask_fraction(cfg)
     fwd_flops = 4.0 * B * H * N * N * d * frac
@@ -529,6 +552,9 @@ def main():
         "parity_vs_oracle": parity,
         "deterministic_rerun": deterministic,
         "clock_mhz": clock,
+        "gemm_reference": gemm,
+        "frac_of_gemm_reference": ({n: v["TFLOP/s"] / gemm["tflops"] for n, v in per_kernel.items()}
+                                   if gemm else None),
         "device": {"name": props.name, "arch": getattr(props, "gcnArchName", ""),
                    "compute_units": props.multi_processor_count},
         "kernel_source_hash": kernel_source_hash(),
