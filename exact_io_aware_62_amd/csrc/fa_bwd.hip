@@ -127,9 +127,14 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
   const int nqt = (Nq + BQ - 1) / BQ;
   const int t_begin = CAUSAL ? max(0, kb * BKB - dlt) / BQ : 0;
   const int mcol = SPARSE ? (kb * BKB) / p.mask_block : 0;
+  MaskWindow mw;
   auto next_tile = [&](int t) FA_INLINE -> int {
     if constexpr (SPARSE) {
-      while (t < nqt && p.blockmask[(size_t)((t * BQ) / p.mask_block) * p.nbm + mcol] == 0) ++t;
+      // column mcol of the mask, one byte per block of query rows
+      t = next_active_tile<BQ>(mw, t, nqt, p.mask_block, (Nq + p.mask_block - 1) / p.mask_block,
+                               [&](int b) FA_INLINE {
+                                 return p.blockmask[(size_t)b * p.nbm + mcol];
+                               });
     } else {
       // opaque to the optimizer: with a visible t + 1 sequence it reshapes
       // the tile loop and the dK / dV accumulators end up copied between
@@ -473,10 +478,12 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   const int kend = CAUSAL ? max(0, min(Nk, (qb + 1) * BQ + dlt)) : Nk;
   const int ntiles = (kend + BK - 1) / BK;
   const int mrow = SPARSE ? (qb * BQ) / p.mask_block : 0;
+  MaskWindow mw;
   auto next_tile = [&](int t) FA_INLINE -> int {
     if constexpr (SPARSE) {
       const uint8_t* mr = p.blockmask + (size_t)mrow * p.nbm;
-      while (t < ntiles && mr[(t * BK) / p.mask_block] == 0) ++t;
+      return next_active_tile<BK>(mw, t, ntiles, p.mask_block, p.nbm,
+                                  [&](int b) FA_INLINE { return mr[b]; });
     }
     return t;
   };

@@ -456,6 +456,48 @@ __device__ __forceinline__ void store_rows_staged(char* stage, const f32x16 (&ac
   __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
 }
 
+// Active blocks of one row (or column) of the block mask, 64 at a time: bit i
+// of `bits` tells whether block base + i is active.  A window is filled with
+// one byte load per lane and a ballot, only when a query moves past the
+// current 64-block window.  The kernels ask right after their per-tile wait
+// and barrier, when no copy is in flight, so that load costs its own latency
+// and nothing more; between refills a query is a few scalar bit operations
+// instead of one dependent mask load per skipped tile.  Wavefront-uniform.
+struct MaskWindow {
+  unsigned long long bits = 0;
+  int base = -64;
+  // first active block >= b among blocks [0, nb), or nb; at(blk) returns the
+  // mask byte of block blk (blk < nb)
+  template <class At>
+  __device__ __forceinline__ int next(int b, int nb, const At& at) {
+    while (b < nb) {
+      const int wb = b & ~63;
+      if (wb != base) {
+        const int lb = wb + lane_id();
+        bits = __builtin_amdgcn_ballot_w64(lb < nb && at(lb) != 0);
+        base = wb;
+      }
+      const unsigned long long m = bits >> (b - wb);
+      if (m) return b + (int)__builtin_ctzll(m);
+      b = wb + 64;
+    }
+    return nb;
+  }
+};
+
+// Next tile t' >= t (tiles of TILE rows along the masked axis) whose mask block
+// is active, or `ntiles`: the block of t itself if active, else the first tile
+// of the next active block.
+template <int TILE, class At>
+__device__ __forceinline__ int next_active_tile(MaskWindow& w, int t, int ntiles, int mask_block,
+                                                int nb, const At& at) {
+  if (t >= ntiles) return ntiles;
+  const int b = (t * TILE) / mask_block;
+  const int b2 = w.next(b, nb, at);
+  if (b2 != b) t = b2 * (mask_block / TILE);
+  return min(t, ntiles);
+}
+
 // Block index -> (query/key block, batch*head).  Workgroups are dispatched
 // round-robin over the 8 XCDs (each with its own L2), so id mod 8 picks the
 // XCD.  Every head's blocks go to one XCD (bh mod 8 = id mod 8), and within an

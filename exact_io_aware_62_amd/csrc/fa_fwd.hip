@@ -105,10 +105,12 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   const int ntiles = SPLIT ? min((kend + BK - 1) / BK, tbeg + p.tiles_per_split)
                            : (kend + BK - 1) / BK;
   const int mrow = SPARSE ? (qb * BQ) / p.mask_block : 0;
+  MaskWindow mw;
   auto next_tile = [&](int t) FA_INLINE -> int {
     if constexpr (SPARSE) {
       const uint8_t* mr = p.blockmask + (size_t)mrow * p.nbm;
-      while (t < ntiles && mr[(t * BK) / p.mask_block] == 0) ++t;
+      return next_active_tile<BK>(mw, t, ntiles, p.mask_block, p.nbm,
+                                  [&](int b) FA_INLINE { return mr[b]; });
     }
     return t;
   };

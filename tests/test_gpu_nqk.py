@@ -32,6 +32,13 @@ CASES = [
     (2, 1, 200, 333, 128, "causal"),
     (1, 2, 130, 260, 64, "blocksparse"),
     (1, 2, 333, 130, 128, "dense"),
+    # more than 64 mask blocks along the axis a kernel walks: the tile skipping reads
+    # the mask 64 blocks at a time and has to move to the next window (keys for the
+    # forward and dQ, queries for dK/dV); sparse rows with active blocks on both
+    # sides of the window edge and long inactive runs
+    (1, 2, 256, 128 * 72, 64, "blocksparse_wide"),
+    (1, 2, 128 * 72, 256, 64, "blocksparse_wide"),
+    (1, 1, 128 * 70 + 50, 128 * 66 + 7, 128, "blocksparse_wide_causal"),
 ]
 
 
@@ -42,12 +49,27 @@ def test_nqk_parity(fa, case):
     B, H, Nq, Nk, d, kind = case
     seed = 500 + Nq + Nk
     bits = synth.draw_inputs_nqk(B, H, Nq, Nk, d, seed)
-    causal = kind == "causal"
+    causal = kind.endswith("causal")
     bm = None
     if kind == "blocksparse":
         bm = (np.random.default_rng(seed).random((-(-Nq // 128), -(-Nk // 128))) < 0.6)
         bm = bm.astype(np.uint8)
         bm[0, 0] = 1
+    elif kind.startswith("blocksparse_wide"):
+        nbq, nbk = -(-Nq // 128), -(-Nk // 128)
+        bm = (np.random.default_rng(seed).random((nbq, nbk)) < 0.08).astype(np.uint8)
+        # blocks just before and after the 64-block window edges, in rows and columns
+        for i in range(nbq):
+            for j in (0, 63, 64, nbk - 1):
+                if j < nbk and (i + j) % 3 == 0:
+                    bm[i, j] = 1
+        for j in range(nbk):
+            for i in (0, 63, 64, nbq - 1):
+                if i < nbq and (i + j) % 2 == 0:
+                    bm[i, j] = 1
+        bm[:, min(nbk - 1, 5):min(nbk, 60)] = 0 if nbk > 66 else bm[:, min(nbk - 1, 5):min(nbk, 60)]
+        if nbq > 66:
+            bm[5:60, :] = 0         # a long run of inactive query blocks in every column
     scale = float(np.float32(d ** -0.5))
     q, k, v, do = (to_gpu(bits[x]) for x in ("q", "k", "v", "do"))
     bmg = mask_to_gpu(bm)
