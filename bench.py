@@ -135,10 +135,13 @@ def sample_clock(run, seconds: float, torch, dev):
         if batches % 8 == 0:      # bound the queue depth
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+    # a reading of 0 means the query failed at that moment, not a stopped clock
+    zeros = sum(1 for x in samples if x <= 0.0)
+    samples = [x for x in samples if x > 0.0]
     if not samples:
         return None
     return {"median": float(np.median(samples)), "min": min(samples), "max": max(samples),
-            "samples": len(samples),
+            "samples": len(samples), "failed_reads": zeros,
             "source": (f"torch.cuda.clock_rate (current graphics clock) read between queued "
                        f"steps over {seconds:.1f} s of back-to-back steps")}
 
