@@ -109,7 +109,8 @@ int check_dropout(float p_drop) {
   return FA_OK;
 }
 
-// The kernels' dropout fields: drop iff the Philox word < floor(p * 2^32);
+// The kernels' dropout fields: drop iff the element's 16-bit Philox half is
+// < floor(p * 2^16);
 // kept values are multiplied by 1 / (1 - p) (fp32), which the kernels apply
 // once to their accumulated outputs.
 void set_dropout_keep(fa::FwdParams&, float) {}
@@ -117,8 +118,8 @@ void set_dropout_keep(fa::BwdParams& p, float p_drop) { p.drop_keep = 1.0f - p_d
 
 template <class Params>
 void set_dropout(Params& p, float p_drop, uint64_t seed, uint32_t offset) {
-  const double t = std::floor((double)p_drop * 4294967296.0);
-  p.drop_thresh = t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+  const double t = std::floor((double)p_drop * 65536.0);
+  p.drop_thresh = t >= 65535.0 ? 0xFFFFu : (uint32_t)t;
   p.drop_scale = 1.0f / (1.0f - p_drop);
   set_dropout_keep(p, p_drop);
   p.seed_lo = (uint32_t)(seed & 0xFFFFFFFFu);

@@ -213,18 +213,33 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
   // key `key`) of the current tile; the next tile's are drawn during the
   // current tile's last step, where the fewest registers are live.
   uint32_t keep_cur = 0xFFFFFFFFu, keep_next = 0xFFFFFFFFu;
-  // draw m for the tile at query q0: this lane draws for query
-  // q0 + 8m + 4g + (r % 4) and keys kw + 4 (r / 4) .. +3; lane r of the quad
-  // then collects bit r % 4 of each quad lane's result
-  auto draw_keep = [&](int q0, int m) FA_INLINE {
-    const uint32_t mine =
-        drs.keep4((uint32_t)((kw >> 2) + (r >> 2)), (uint32_t)(q0 + 8 * m + 4 * g + (r & 3)));
-    const int sh = r & 3;
-    const uint32_t bits = ((quad_bcast<0>(mine) >> sh) & 1u) |
-                          (((quad_bcast<1>(mine) >> sh) & 1u) << 1) |
-                          (((quad_bcast<2>(mine) >> sh) & 1u) << 2) |
-                          (((quad_bcast<3>(mine) >> sh) & 1u) << 3);
-    keep_next = (keep_next & ~(0xFu << (4 * m))) | (bits << (4 * m));
+  // A quad of lanes holds four consecutive keys (key group (kw + r) / 4) and,
+  // per lane group g, the 16 queries of registers i (query q0 + (i/4)*8 +
+  // g*4 + i%4), eight query pairs p = (i/4)*2 + (i%4)/2.  One draw decides a
+  // pair for the quad's four keys.  Lane c = r % 4 draws pairs c (h = 0) and
+  // c + 4 (h = 1) of the tile at query q0; finish_keep then collects, from
+  // each quad lane's two draws, the bits of this lane's key.
+  uint32_t keep_mine = 0;
+  auto draw_keep = [&](int q0, int h) FA_INLINE {
+    const int pr = (r & 3) + 4 * h;
+    const uint32_t ig = (uint32_t)((q0 + (pr >> 1) * 8 + g * 4 + (pr & 1) * 2) >> 1);
+    keep_mine |= drs.keep8((uint32_t)((kw >> 2) + (r >> 2)), ig) << (8 * h);
+    pin(keep_mine);
+  };
+  auto finish_keep = [&]() FA_INLINE {
+    const int c = r & 3;
+    uint32_t kb = 0;
+    static_for<0, 4>([&](auto tc) FA_INLINE {
+      constexpr int T = decltype(tc)::value;
+      // lane T's draws: pair T in bits 0..7, pair T + 4 in bits 8..15; this
+      // key's bits c and 4 + c of each go to registers i0, i0 + 1 and
+      // i0 + 8, i0 + 9
+      constexpr int i0 = (T >> 1) * 4 + (T & 1) * 2;
+      const uint32_t y = (quad_bcast<T>(keep_mine) >> c) & 0x1111u;
+      kb |= ((y & 0x101u) | ((y >> 3) & 0x202u)) << i0;
+    });
+    keep_next = kb;
+    keep_mine = 0;
     pin(keep_next);
   };
 
@@ -334,8 +349,9 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
       dk[j % NDB] = mfma32x32x16(fa[j], sb[j / NDB], dk[j % NDB]);
       if (j + PF < NJ) fa[j + PF] = tr_read(qt, j + PF);
       if constexpr (DROPOUT) {
-        // the next tile's four draws (unused after the last tile)
-        if (j % (NJ / 4) == 0) draw_keep(tn * BQ, j / (NJ / 4));
+        // the next tile's two draws (unused after the last tile)
+        if (j % (NJ / 2) == 0) draw_keep(tn * BQ, j / (NJ / 2));
+        if (j == NJ - 1) finish_keep();
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -348,8 +364,9 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
     issue(t, 0);
     finish_issue(0);
     if constexpr (DROPOUT) {
-#pragma unroll
-      for (int m = 0; m < 4; ++m) draw_keep(t * BQ, m);
+      draw_keep(t * BQ, 0);
+      draw_keep(t * BQ, 1);
+      finish_keep();
     }
   }
   // one loop body for both stages keeps the dK / dV accumulators in one
@@ -535,7 +552,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     s[0] = zero16(); s[1] = zero16(); dp[0] = zero16(); dp[1] = zero16();
     // keep bits: bit kb*16 + i for register i of key block kb (keys
     // k0 + kb*32 + (i/4)*8 + g*4 + i%4 of this lane's row)
-    uint32_t keepbits = 0xFFFFFFFFu;
+    uint32_t keepbits = 0xFFFFFFFFu, keep_give = 0;
     bf16x8 fr[NS];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -553,13 +570,27 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
         dq[db] = mfma32x32x16(fr[j], ds[kb * 2 + ks2], dq[db]);
       }
       if constexpr (j + PF < NS) fr[j + PF] = operand(kt, vt, j + PF);
-      if constexpr (DROPOUT && j < 2 * NKK && j % (2 * NKK / 8) == 0) {
-        // eight draws per tile, spread over the S^T products
-        constexpr int u = j / (2 * NKK / 8), kb = u >> 2, m = u & 3;
-        const uint32_t bits = drs.keep4((uint32_t)(t * (BK / 4) + kb * 8 + m * 2 + g),
-                                        (uint32_t)qrow);
-        keepbits = (keepbits & ~(0xFu << (4 * u))) | (bits << (4 * u));
+      if constexpr (DROPOUT && j < 2 * NKK && j % (2 * NKK / 4) == 0) {
+        // four draws per tile, spread over the S^T products.  One draw decides
+        // four keys of this lane's row and of lane r ^ 1's (rows 2 ig, 2 ig + 1:
+        // q0w is even); draw v takes key group u = 2v + (row parity), keep bits
+        // 4u .. 4u+3 (keys k0 + kb*32 + m*8 + g*4 + 0..3, u = kb*4 + m).
+        constexpr int v = j / (2 * NKK / 4);
+        const int odd = qrow & 1;
+        const int u = 2 * v + odd, kb = u >> 2, m = u & 3;
+        const uint32_t bits =
+            drs.keep8((uint32_t)(t * (BK / 4) + kb * 8 + m * 2 + g), (uint32_t)qrow >> 1);
+        const uint32_t own = ((odd ? bits >> 4 : bits) & 0xFu) << (4 * u);
+        const uint32_t give = ((odd ? bits : bits >> 4) & 0xFu) << (4 * u);
+        keepbits = v == 0 ? own : keepbits | own;
+        keep_give = v == 0 ? give : keep_give | give;
         pin(keepbits);
+        pin(keep_give);
+        if constexpr (v == 3) {
+          // the other row's bits come from the pair's other lane
+          keepbits |= pair_swap(keep_give);
+          pin(keepbits);
+        }
       }
       // vector work of this product slot: unit u in 0..3 (P of block 0, P of
       // block 1, dS of block 0, dS of block 1) runs in slots

@@ -136,17 +136,31 @@ __device__ __forceinline__ u32x4 philox4x32_10(uint32_t c0, uint32_t c1, uint32_
   return out;
 }
 
-// Dropout stream of one head: element (i, j) is kept iff word j % 4 of
-// philox4x32_10(j / 4, i, bh, offset; seed) is >= thresh.  keep4 returns the
-// keep bits of keys 4*jg .. 4*jg+3 of query i in bits 0..3.
+// Dropout stream of one head.  One Philox draw, on the counter
+// (j / 4, i / 2, bh, offset), decides the block of queries i = 2 ig, 2 ig + 1 and
+// keys j = 4 jg .. 4 jg + 3: element e = 4 (i % 2) + j % 4 of the block takes the
+// 16-bit half e % 2 (low half first) of output word e / 2, and is kept iff that
+// value is >= thresh (floor(p 2^16)).  keep8 returns the block's keep bits, bit e
+// for element e: bits 0..3 are query 2 ig, bits 4..7 query 2 ig + 1.
 struct DropoutStream {
   uint32_t seed_lo, seed_hi, bh, offset, thresh;
-  __device__ __forceinline__ uint32_t keep4(uint32_t jg, uint32_t i) const {
-    const u32x4 w = philox4x32_10(jg, i, bh, offset, seed_lo, seed_hi);
-    return (uint32_t)(w[0] >= thresh) | ((uint32_t)(w[1] >= thresh) << 1) |
-           ((uint32_t)(w[2] >= thresh) << 2) | ((uint32_t)(w[3] >= thresh) << 3);
+  __device__ __forceinline__ uint32_t keep8(uint32_t jg, uint32_t ig) const {
+    const u32x4 w = philox4x32_10(jg, ig, bh, offset, seed_lo, seed_hi);
+    uint32_t bits = 0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t h = (e & 1) ? (w[e >> 1] >> 16) : (w[e >> 1] & 0xFFFFu);
+      bits |= (uint32_t)(h >= thresh) << e;
+    }
+    return bits;
   }
 };
+
+// Value of lane l ^ 1 (DPP quad permute 1, 0, 3, 2).
+__device__ __forceinline__ uint32_t pair_swap(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 1 | (0 << 2) | (3 << 4) | (2 << 6), 0xF, 0xF,
+                                            false);
+}
 
 // Value of lane t (0..3) of this lane's group of four (DPP quad permute).
 template <int T>

@@ -135,11 +135,29 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     ds_.offset = p.drop_offset;
     ds_.thresh = p.drop_thresh;
   }
-  // keys k0 + kb*32 + m*8 + g*4 + 0..3 of this lane's row, for call u = kb*4 + m
-  auto draw_keep = [&](int tc, int u) FA_INLINE {
-    const int kb = u >> 2, m = u & 3;
-    const uint32_t bits = ds_.keep4((uint32_t)(tc * (BK / 4) + kb * 8 + m * 2 + g), (uint32_t)qrow);
-    keepbits = (keepbits & ~(0xFu << (4 * u))) | (bits << (4 * u));
+  // One draw decides four keys of this lane's row and of the row of lane
+  // r ^ 1 (rows 2 ig, 2 ig + 1: q0w is even).  Key group u = kb*4 + m (keys
+  // k0 + kb*32 + m*8 + g*4 + 0..3, keep bits 4u .. 4u+3) is drawn by the lane
+  // of the pair whose row parity equals u's: draw v of a tile takes group
+  // u = 2v + (r & 1).  The bits for the other row are handed over with one
+  // lane swap once the tile's four draws are made.  The previous tile's bits
+  // are dead by then (its P was packed in the previous iteration), so this
+  // lane's own bits collect in keepbits directly.
+  uint32_t keep_give = 0;
+  auto draw_keep = [&](int tc, int v) FA_INLINE {
+    const int odd = qrow & 1;
+    const int u = 2 * v + odd, kb = u >> 2, m = u & 3;
+    const uint32_t bits =
+        ds_.keep8((uint32_t)(tc * (BK / 4) + kb * 8 + m * 2 + g), (uint32_t)qrow >> 1);
+    const uint32_t own = ((odd ? bits >> 4 : bits) & 0xFu) << (4 * u);
+    const uint32_t give = ((odd ? bits : bits >> 4) & 0xFu) << (4 * u);
+    keepbits = v == 0 ? own : keepbits | own;
+    keep_give = v == 0 ? give : keep_give | give;
+    pin(keepbits);
+    pin(keep_give);
+  };
+  auto finish_keep = [&]() FA_INLINE {
+    keepbits |= pair_swap(keep_give);
     pin(keepbits);
   };
   // P as it enters the P V product: kept, or 0 (1 / (1 - p) comes at the end)
@@ -358,8 +376,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       sc[j & 1] = mfma32x32x16(kfr[j], qf[j >> 1], sc[j & 1]);
       if (j + PF < NJ) kread(j + PF);
       if constexpr (DROPOUT) {
-        // eight draws per tile, spread over the score products
-        if (j % (NJ / 8) == 0) draw_keep(tc, j / (NJ / 8));
+        // four draws per tile, spread over the score products
+        if (j % (NJ / 4) == 0) draw_keep(tc, j / (NJ / 4));
+        if (j == NJ - 1) finish_keep();
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -546,30 +565,35 @@ hipError_t launch_fwd(const FwdParams& p, int d, bool causal, bool sparse, bool 
 }
 
 // Keep mask of the dropout stream, keep[bh][i][j] = 1 or 0, for inspection and
-// tests: one thread per four keys of one query (one Philox draw).
+// tests: one thread per block of two queries and four keys (one Philox draw).
 __global__ __launch_bounds__(256) void dropout_keep_mask_kernel(FwdParams p, uint8_t* keep,
                                                                long long groups) {
   const long long gid = (long long)blockIdx.x * 256 + threadIdx.x;
   if (gid >= groups) return;
-  const int ng = (p.Nk + 3) / 4;
-  const long long row = gid / ng;            // bh * Nq + i
-  const int jg = (int)(gid - row * ng);
-  const int bh = (int)(row / p.Nq), i = (int)(row - (long long)bh * p.Nq);
+  const int ng = (p.Nk + 3) / 4, nig = (p.Nq + 1) / 2;
+  const long long bhig = gid / ng;           // bh * nig + ig
+  const int jg = (int)(gid - bhig * ng);
+  const int bh = (int)(bhig / nig), ig = (int)(bhig - (long long)bh * nig);
   DropoutStream ds;
   ds.seed_lo = p.seed_lo;
   ds.seed_hi = p.seed_hi;
   ds.bh = (uint32_t)bh;
   ds.offset = p.drop_offset;
   ds.thresh = p.drop_thresh;
-  const uint32_t bits = ds.keep4((uint32_t)jg, (uint32_t)i);
-  uint8_t* out = keep + row * p.Nk + 4 * jg;
+  const uint32_t bits = ds.keep8((uint32_t)jg, (uint32_t)ig);
 #pragma unroll
-  for (int t = 0; t < 4; ++t)
-    if (4 * jg + t < p.Nk) out[t] = (uint8_t)((bits >> t) & 1u);
+  for (int h = 0; h < 2; ++h) {
+    const int i = 2 * ig + h;
+    if (i >= p.Nq) break;
+    uint8_t* out = keep + ((long long)bh * p.Nq + i) * p.Nk + 4 * jg;
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      if (4 * jg + t < p.Nk) out[t] = (uint8_t)((bits >> (4 * h + t)) & 1u);
+  }
 }
 
 hipError_t launch_dropout_keep_mask(const FwdParams& p, uint8_t* keep, hipStream_t stream) {
-  const long long groups = (long long)p.BH * p.Nq * ((p.Nk + 3) / 4);
+  const long long groups = (long long)p.BH * ((p.Nq + 1) / 2) * ((p.Nk + 3) / 4);
   const long long blocks = (groups + 255) / 256;
   hipLaunchKernelGGL(dropout_keep_mask_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, p,
                      keep, groups);

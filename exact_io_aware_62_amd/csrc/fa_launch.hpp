@@ -26,8 +26,9 @@ struct FwdParams {
   float* Opart;
   float* LSEpart;
   // dropout on P (read only by the dropout kernels): element (i, j) of head bh
-  // is kept iff philox4x32_10(j/4, i, bh, drop_offset; seed)[j % 4] >= drop_thresh
-  uint32_t drop_thresh;      // floor(p * 2^32)
+  // is kept iff 16-bit half e % 2 of philox4x32_10(j/4, i/2, bh, drop_offset;
+  // seed)[e / 2], e = 4 (i % 2) + j % 4, is >= drop_thresh
+  uint32_t drop_thresh;      // floor(p * 2^16)
   float drop_scale;          // 1 / (1 - p): the kept probabilities' factor, applied to O at the end
   uint32_t seed_lo, seed_hi, drop_offset;
 };
@@ -53,8 +54,9 @@ struct BwdParams {
   float scale;               // softmax scale
   float scale_log2;          // scale * log2(e)
   // dropout on P (read only by the dropout kernels): element (i, j) of head bh
-  // is kept iff philox4x32_10(j/4, i, bh, drop_offset; seed)[j % 4] >= drop_thresh
-  uint32_t drop_thresh;      // floor(p * 2^32)
+  // is kept iff 16-bit half e % 2 of philox4x32_10(j/4, i/2, bh, drop_offset;
+  // seed)[e / 2], e = 4 (i % 2) + j % 4, is >= drop_thresh
+  uint32_t drop_thresh;      // floor(p * 2^16)
   float drop_scale;          // 1 / (1 - p), applied to dV, dK and dQ at the end
   float drop_keep;           // 1 - p: D is taken times this inside the loops
   uint32_t seed_lo, seed_hi, drop_offset;

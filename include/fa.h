@@ -272,10 +272,13 @@ size_t fa_fwd_splitkv_workspace_bytes(int B, int H, int Nq, int Nk, int d, int n
  *   P = softmax(scale * Q K^T + mask) as in fa_fwd; LSE is P's (no dropout);
  *   O = (P * keep / (1 - p_drop)) V.
  *
- * Element (b, h, i, j) is kept iff word (j mod 4) of Philox4x32-10 (Salmon et
- * al., "Parallel random numbers: as easy as 1, 2, 3", SC 2011) on the counter
- * (j / 4, i, b * H + h, offset) under the key (seed mod 2^32, seed / 2^32) is
- * >= floor(p_drop * 2^32).  The same (p_drop, seed, offset) must be passed to
+ * One draw of Philox4x32-10 (Salmon et al., "Parallel random numbers: as easy
+ * as 1, 2, 3", SC 2011) on the counter (j / 4, i / 2, b * H + h, offset) under
+ * the key (seed mod 2^32, seed / 2^32) decides the two queries i and four keys
+ * j that share those quotients: element (b, h, i, j) takes the 16-bit half
+ * e mod 2 (low half first) of output word e / 2, e = 4 (i mod 2) + (j mod 4),
+ * and is kept iff that value is >= floor(p_drop * 2^16).  The same
+ * (p_drop, seed, offset) must be passed to
  * fa_bwd_dropout; a caller takes a fresh offset (or seed) per call to get a
  * fresh mask.  p_drop must satisfy 0 <= p_drop < 1 (else FA_ERR_UNSUPPORTED);
  * p_drop = 0 gives exactly fa_fwd / fa_bwd.  Other arguments and errors are

@@ -24,6 +24,7 @@ from .attention import (  # noqa: F401
 from .dropout import (  # noqa: F401
     philox4x32_10,
     drop_threshold,
+    draw_halves,
     keep_mask,
     head_forward_dropout,
     head_backward_dropout,

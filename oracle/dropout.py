@@ -15,10 +15,14 @@ backward can regenerate the forward's mask instead of storing it:
   D_i = sum_j P_ij dP_ij (which equals sum_k dO_ik O_ik);  dS = P * (dP - D);
   dQ = scale * dS K;  dK = scale * dS^T Q.
 
-The draw for element (b, h, i, j) is word j mod 4 of Philox4x32-10 (Salmon, Moraes,
-Dror and Shaw, "Parallel random numbers: as easy as 1, 2, 3", SC 2011) applied to the
-counter (j div 4, i, b*H + h, offset) under the key (seed mod 2^32, seed div 2^32);
-the element is dropped iff that word is below floor(p * 2^32).  Philox is written here
+One draw of Philox4x32-10 (Salmon, Moraes, Dror and Shaw, "Parallel random numbers:
+as easy as 1, 2, 3", SC 2011), applied to the counter (j div 4, i div 2, b*H + h,
+offset) under the key (seed mod 2^32, seed div 2^32), decides the block of two
+queries i and four keys j that share those quotients: its four 32-bit output words
+hold eight 16-bit halves, and element (b, h, i, j) takes half number
+e = 4 (i mod 2) + (j mod 4), i.e. bits 16 (e mod 2) .. 16 (e mod 2) + 15 of word
+e div 2.  The element is dropped iff that 16-bit value is below floor(p * 2^16).
+Philox is written here
 from its definition in that paper: ten rounds, each multiplying counter words 0 and 2
 by two fixed odd constants and mixing the high and low halves of the products with
 words 1 and 3 and the round key, the key advancing by two Weyl constants per round.
@@ -58,22 +62,30 @@ def philox4x32_10(c0, c1, c2, c3, k0: int, k1: int):
 
 
 def drop_threshold(p: float) -> int:
-    """floor(p * 2^32), the 32-bit draw below which an element is dropped."""
+    """floor(p * 2^16), the 16-bit value below which an element is dropped."""
     if not 0.0 <= p < 1.0:
         raise ValueError("dropout probability must be in [0, 1)")
-    return min(int(math.floor(float(p) * 4294967296.0)), _MASK32)
+    return min(int(math.floor(float(p) * 65536.0)), 0xFFFF)
+
+
+def draw_halves(n_q: int, n_k: int, bh: int, seed: int, offset: int) -> np.ndarray:
+    """uint64 [n_q, n_k]: the 16-bit draw of each element (i, j) of head bh."""
+    ig = np.arange((n_q + 1) // 2, dtype=np.uint64)[:, None]
+    jg = np.arange((n_k + 3) // 4, dtype=np.uint64)[None, :]
+    shape = ((n_q + 1) // 2, (n_k + 3) // 4)
+    words = philox4x32_10(np.broadcast_to(jg, shape), np.broadcast_to(ig, shape),
+                          np.full(shape, bh, np.uint64), np.full(shape, offset, np.uint64),
+                          seed & _MASK32, (seed >> 32) & _MASK32)
+    out = np.empty((shape[0], 2, shape[1], 4), np.uint64)   # [i div 2, i mod 2, j div 4, j mod 4]
+    for e in range(8):
+        half = (words[e // 2] >> np.uint64(16 * (e % 2))) & np.uint64(0xFFFF)
+        out[:, e // 4, :, e % 4] = half
+    return out.reshape(2 * shape[0], 4 * shape[1])[:n_q, :n_k]
 
 
 def keep_mask(n_q: int, n_k: int, bh: int, p: float, seed: int, offset: int) -> np.ndarray:
     """Boolean [n_q, n_k]: True where element (i, j) of head bh is kept."""
-    i = np.arange(n_q, dtype=np.uint64)[:, None]
-    jg = np.arange((n_k + 3) // 4, dtype=np.uint64)[None, :]
-    shape = (n_q, (n_k + 3) // 4)
-    words = philox4x32_10(np.broadcast_to(jg, shape), np.broadcast_to(i, shape),
-                          np.full(shape, bh, np.uint64), np.full(shape, offset, np.uint64),
-                          seed & _MASK32, (seed >> 32) & _MASK32)
-    draws = np.stack(words, axis=-1).reshape(n_q, -1)[:, :n_k]   # word j % 4 of group j // 4
-    return draws >= np.uint64(drop_threshold(p))
+    return draw_halves(n_q, n_k, bh, seed, offset) >= np.uint64(drop_threshold(p))
 
 
 def head_forward_dropout(q, k, v, scale: float, allowed: np.ndarray, p: float,

@@ -43,26 +43,23 @@ def test_keep_mask_bitwise(fa, B, H, N, p, seed, offset):
         assert np.array_equal(keep.reshape(B * H, N, N)[bh].astype(bool), ref), bh
 
 
-def _p_bracket(w: int):
-    """float32 probabilities p_keep, p_drop whose thresholds floor(p * 2^32) lie just
-    at or below the 32-bit word w and just above it."""
-    two32 = 4294967296.0
-    lo = np.float32(w / two32)
-    while int(np.floor(float(lo) * two32)) > w:
-        lo = np.nextafter(lo, np.float32(0))
-    hi = np.float32((w + 1) / two32)
-    while int(np.floor(float(hi) * two32)) <= w:
-        hi = np.nextafter(hi, np.float32(1))
+def _p_bracket(h: int):
+    """float32 probabilities p_keep, p_drop whose thresholds floor(p * 2^16) are just
+    h (keep a 16-bit draw h) and h + 1 (drop it)."""
+    lo = np.float32(h / 65536.0)
+    hi = np.float32((h + 1) / 65536.0)
+    assert int(np.floor(float(lo) * 65536.0)) == h
+    assert int(np.floor(float(hi) * 65536.0)) == h + 1
     return float(lo), float(hi)
 
 
 def test_keep_bits_follow_published_philox_words(fa):
-    """Query 0, keys 0..3 of head 0 with seed 0 and offset 0 are the four words of
-    Philox4x32-10 on the zero counter under the zero key, whose published values are
-    in tests/golden/philox_kat.json.  For each word w, a threshold just at or below w
-    keeps the element and one just above drops it: the GPU generator is pinned to
-    the published output independently of the oracle (to within the float32
-    spacing of p, a few hundred units of 2^-32)."""
+    """Queries 0, 1 and keys 0..3 of head 0 with seed 0 and offset 0 form the block of
+    the zero counter under the zero key, whose published output words are in
+    tests/golden/philox_kat.json.  Element (i, j) takes 16-bit half e mod 2 of word
+    e div 2, e = 4 i + j.  For each element, the threshold equal to its half keeps
+    it and the next one drops it: the GPU generator and its half-word layout are
+    pinned to the published output independently of the oracle."""
     import json
     import os
     torch = torch_mod()
@@ -70,13 +67,18 @@ def test_keep_bits_follow_published_philox_words(fa):
         vec = json.load(f)["vectors"][0]
     assert vec["counter"] == ["00000000"] * 4 and vec["key"] == ["00000000"] * 2
     words = [int(x, 16) for x in vec["output"]]
-    for t, w in enumerate(words):
-        p_keep, p_drop = _p_bracket(w)
-        kept = fa.dropout_keep_mask(1, 1, 4, p_keep, 0, 0).cpu().numpy().reshape(4, 4)
-        dropped = fa.dropout_keep_mask(1, 1, 4, p_drop, 0, 0).cpu().numpy().reshape(4, 4)
-        torch.cuda.synchronize()
-        assert kept[0, t] == 1, (t, hex(w), p_keep)
-        assert dropped[0, t] == 0, (t, hex(w), p_drop)
+    for i in range(2):
+        for j in range(4):
+            e = 4 * i + j
+            h = (words[e // 2] >> (16 * (e % 2))) & 0xFFFF
+            if h == 0xFFFF:
+                continue   # no p < 1 drops the largest draw
+            p_keep, p_drop = _p_bracket(h)
+            kept = fa.dropout_keep_mask(1, 1, 4, p_keep, 0, 0).cpu().numpy().reshape(4, 4)
+            dropped = fa.dropout_keep_mask(1, 1, 4, p_drop, 0, 0).cpu().numpy().reshape(4, 4)
+            torch.cuda.synchronize()
+            assert kept[i, j] == 1, (i, j, hex(h), p_keep)
+            assert dropped[i, j] == 0, (i, j, hex(h), p_drop)
 
 
 CASES = [

@@ -174,9 +174,36 @@ def test_keep_mask_prefix_property_and_threshold():
     assert np.array_equal(oracle.keep_mask(133, 70, 5, 0.3, 7, 9), big[:133, :70])
     assert oracle.keep_mask(64, 64, 0, 0.0, 1, 1).all()
     assert oracle.drop_threshold(0.0) == 0
-    assert oracle.drop_threshold(0.5) == 2**31
+    assert oracle.drop_threshold(0.5) == 2**15
+    assert oracle.drop_threshold(0.99999999) == 0xFFFF
     with pytest.raises(ValueError):
         oracle.drop_threshold(1.0)
+
+
+def test_draw_halves_take_the_published_zero_counter_output():
+    """Queries 0, 1 and keys 0..3 of head 0 with seed 0 and offset 0 form the block of
+    the zero counter under the zero key: its eight 16-bit draws are the halves of the
+    published output words, element (i, j) taking half (e mod 2) of word (e div 2)
+    with e = 4 i + j (low half first)."""
+    _, c, k, r = _kat_vectors()[0]
+    assert c == [0, 0, 0, 0] and k == [0, 0]
+    got = oracle.draw_halves(2, 4, 0, 0, 0)
+    for i in range(2):
+        for j in range(4):
+            e = 4 * i + j
+            assert int(got[i, j]) == (r[e // 2] >> (16 * (e % 2))) & 0xFFFF, (i, j)
+
+
+def test_draw_halves_match_a_scalar_reading_of_the_rule():
+    """Every element of a ragged head, from the scalar Philox on its own block counter
+    (j div 4, i div 2, bh, offset) and the half e = 4 (i mod 2) + (j mod 4)."""
+    n_q, n_k, bh, seed, offset = 7, 10, 3, (5 << 32) + 11, 42
+    got = oracle.draw_halves(n_q, n_k, bh, seed, offset)
+    for i in range(n_q):
+        for j in range(n_k):
+            w = _philox_scalar([j // 4, i // 2, bh, offset], [seed % 2**32, seed >> 32])
+            e = 4 * (i % 2) + (j % 4)
+            assert int(got[i, j]) == (w[e // 2] >> (16 * (e % 2))) & 0xFFFF, (i, j)
 
 
 # ---------------------------------------------------------------- semantics ------
