@@ -78,13 +78,13 @@ __global__ __launch_bounds__(256) void dsum_kernel(BwdParams p, long long rows) 
 //    computed as dV = (1 / (1 - p)) (P keep)^T dO and dS = (1 / (1 - p)) P (dP keep -
 //    D (1 - p)): the loop only zeroes dropped elements and takes D times 1 - p,
 //    and the factor 1 / (1 - p) is applied to dV and dK once, at the store.
-//    A lane holds one key and 16 queries, while one Philox draw covers four
-//    consecutive keys of one query; so the four lanes of a quad (keys
-//    4c .. 4c+3) each draw for a different query and exchange the 4-bit
-//    results with DPP quad permutes: four draws per tile instead of sixteen.
+//    A lane holds one key and 16 queries, while one Philox draw covers two
+//    consecutive queries by four consecutive keys; so the four lanes of a
+//    quad (keys 4c .. 4c+3) each draw two query pairs and exchange the 8-bit
+//    results with DPP quad broadcasts: two draws per lane and tile.
 //    The dropout draws need registers beyond the 256 the d=128 kernel fills;
-//    that instantiation spills 14-23 of them to scratch, which measured 12%
-//    faster than one workgroup per CU without spills.
+//    that instantiation spills 2-6 of them to scratch, which measured faster
+//    than one workgroup per CU without spills.
 template <int D, bool CAUSAL, bool SPARSE, bool DROPOUT>
 __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
   constexpr int BKB = 128, BQ = 32, NW = 4;
