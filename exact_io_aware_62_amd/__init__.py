@@ -82,6 +82,15 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise RuntimeError(
             f"libfa.so not found at {path}; build it with `python -m exact_io_aware_62_amd.build`")
+    # torch ships its own HIP runtime, with the same soname as the system's but
+    # linked by file name.  Loaded first, it satisfies libfa's dependency, so
+    # libfa and torch share one runtime and torch's streams are valid in libfa;
+    # loaded after libfa, it would bring a second runtime and launches on
+    # torch's streams would fail.
+    try:
+        import torch  # noqa: F401
+    except ImportError:
+        pass
     lib = ctypes.CDLL(path)
     for name, (res, args) in _SIGNATURES.items():
         fn = getattr(lib, name)
