@@ -271,10 +271,20 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   // lane-dependent offsets are loop-invariant; with compile-time buffers
   // the compiler keeps them in registers and folds the rest into the
   // instruction's immediate offset.
+  // The lane parts of those reads, one per output column block and half,
+  // computed once (xad is opaque, so the compiler keeps them in registers
+  // instead of redoing the add for every read); the buffer, key block and
+  // k-step offsets then fold into each read's immediate offset.
+  int vofs[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) {
+    vofs[db][0] = xad(oa.xt, db << 6, oa.at0);
+    vofs[db][1] = xad(oa.xt, db << 6, oa.at1);
+  }
   auto vread = [&](const char* vt, int j) FA_INLINE {
     const int kb = j / (2 * NDB), ks2 = (j / NDB) & 1, db = j % NDB;
-    const char* vk = vt + (kb * 32 + 16 * ks2) * RB + (oa.xt ^ (db << 6));
-    return bf16x8_from_halves(lds_tr_b64(vk + oa.at0), lds_tr_b64(vk + oa.at1));
+    const char* vk = vt + (kb * 32 + 16 * ks2) * RB;
+    return bf16x8_from_halves(lds_tr_b64(vk + vofs[db][0]), lds_tr_b64(vk + vofs[db][1]));
   };
   // phase B: O += P_prev V_prev on the matrix cores, interleaved with the
   // current tile's softmax: its row max under the first products, then
