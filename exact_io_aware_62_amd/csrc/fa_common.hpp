@@ -189,13 +189,28 @@ __device__ __forceinline__ void pin(T& x) {
   asm volatile("" : "+v"(x));
 }
 
+// Two- and three-input maxima as single v_max_f32 / v_max3_f32.  fmaxf on
+// values the compiler cannot prove canonical (matrix-core results, lane
+// exchanges) first canonicalises each input, one more instruction per input,
+// and it may regroup a tree of fmaxf; none of these values is a signalling NaN.
+__device__ __forceinline__ float max_raw(float a, float b) {
+  float r;
+  asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
 // max over lanes l and l ^ 32 (the two halves of a wavefront), without LDS:
 // v_permlane32_swap exchanges the upper half of one operand with the lower
 // half of the other, so the two results are {x[l], x[l ^ 32]} in some order.
 __device__ __forceinline__ float max_xor32(float x) {
   const unsigned u = __float_as_uint(x);
   const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max_raw(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 __device__ __forceinline__ float sum_xor32(float x) {

@@ -224,26 +224,27 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
           if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) sc[kb][i] = -INFINITY;
     }
   };
-  // Row max of the tile as a tree of max3 (depth 4 instead of a chain of 16),
-  // in two parts so that each part fits under one matrix product.
+  // Row max of the tile as a tree of three-input maxima (depth 4 instead of a
+  // chain of 16), in two parts so that each part fits under one matrix
+  // product: 32 values -> 12 -> 4 in part 1, then 4 -> 1 and the exchange
+  // with the other lane half in part 2.  Raw max instructions: no
+  // canonicalising of the products' results, no regrouping.
   float mx4[4];
-  // (Only three-input maxima: a two-input maximum of raw products costs two
-  // extra canonicalising instructions.)
   auto rowmax_part1 = [&]() FA_INLINE {
-    float t[10];
+    float t[12];
 #pragma unroll
     for (int u = 0; u < 10; ++u) {
       const int e = 3 * u;
-      t[u] = __builtin_fmaxf(__builtin_fmaxf(sc[e >> 4][e & 15], sc[(e + 1) >> 4][(e + 1) & 15]),
-                             sc[(e + 2) >> 4][(e + 2) & 15]);
+      t[u] = max3_raw(sc[e >> 4][e & 15], sc[(e + 1) >> 4][(e + 1) & 15],
+                      sc[(e + 2) >> 4][(e + 2) & 15]);
     }
+    t[10] = sc[1][14];
+    t[11] = sc[1][15];
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      mx4[u] = __builtin_fmaxf(__builtin_fmaxf(t[3 * u], t[3 * u + 1]), t[3 * u + 2]);
+    for (int u = 0; u < 4; ++u) {
+      mx4[u] = max3_raw(t[3 * u], t[3 * u + 1], t[3 * u + 2]);
       pin(mx4[u]);
     }
-    mx4[3] = __builtin_fmaxf(__builtin_fmaxf(t[9], sc[1][14]), sc[1][15]);
-    pin(mx4[3]);
   };
   // The running maximum only moves when a score exceeds it by more than
   // kSlack (log2 units): every exp2 argument then stays below kSlack, far
@@ -252,7 +253,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   // units this rescales O about once per row.  Returns the factor the
   // accumulated O must be scaled by (1 if unmoved).
   auto rowmax_part2 = [&]() FA_INLINE -> float {
-    const float mx = __builtin_fmaxf(__builtin_fmaxf(mx4[0], mx4[1]), __builtin_fmaxf(mx4[2], mx4[3]));
+    const float mx = max_raw(max3_raw(mx4[0], mx4[1], mx4[2]), mx4[3]);
     const float mxc = max_xor32(mx) * c;
     float alpha = 1.f;
     if (mxc > m_run + kSlack) {

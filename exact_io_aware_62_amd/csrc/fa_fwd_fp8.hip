@@ -156,27 +156,29 @@ __global__ __launch_bounds__(256, 2) void fwd_fp8_kernel(FwdParams p) {
           if (kb * 32 + (i >> 2) * 8 + (i & 3) > lim) sc[kb][i] = -INFINITY;
     }
   };
+  // Row max as in the bf16 forward: 32 values -> 12 -> 4 in part 1, then
+  // 4 -> 1 and the lane-half exchange in part 2, with raw max instructions.
   float mx4[4];
   auto rowmax_part1 = [&]() FA_INLINE {
-    float t[10];
+    float t[12];
 #pragma unroll
     for (int u = 0; u < 10; ++u) {
       const int e = 3 * u;
-      t[u] = __builtin_fmaxf(__builtin_fmaxf(sc[e >> 4][e & 15], sc[(e + 1) >> 4][(e + 1) & 15]),
-                             sc[(e + 2) >> 4][(e + 2) & 15]);
+      t[u] = max3_raw(sc[e >> 4][e & 15], sc[(e + 1) >> 4][(e + 1) & 15],
+                      sc[(e + 2) >> 4][(e + 2) & 15]);
     }
+    t[10] = sc[1][14];
+    t[11] = sc[1][15];
 #pragma unroll
-    for (int u = 0; u < 3; ++u) {
-      mx4[u] = __builtin_fmaxf(__builtin_fmaxf(t[3 * u], t[3 * u + 1]), t[3 * u + 2]);
+    for (int u = 0; u < 4; ++u) {
+      mx4[u] = max3_raw(t[3 * u], t[3 * u + 1], t[3 * u + 2]);
       pin(mx4[u]);
     }
-    mx4[3] = __builtin_fmaxf(__builtin_fmaxf(t[9], sc[1][14]), sc[1][15]);
-    pin(mx4[3]);
   };
   // Moves the running maximum only when the tile's exceeds it by more than
   // kSlack; returns the factor for the accumulated O (1 if unmoved).
   auto rowmax_part2 = [&]() FA_INLINE -> float {
-    const float mx = __builtin_fmaxf(__builtin_fmaxf(mx4[0], mx4[1]), __builtin_fmaxf(mx4[2], mx4[3]));
+    const float mx = max_raw(max3_raw(mx4[0], mx4[1], mx4[2]), mx4[3]);
     const float mxc = max_xor32(mx) * c;
     float alpha = 1.f;
     if (mxc > m_run + kSlack) {
