@@ -96,8 +96,8 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
   // per-query lse2 / D values.  The tiles are filled by copy_async, and the
   // stage is chosen at run time, so one loop body serves both stages.
   __shared__ __attribute__((aligned(1024))) char kbuf[TK::kBytes];
-  __shared__ __attribute__((aligned(1024))) char qbuf[2 * TQ::kBytes];
-  __shared__ __attribute__((aligned(1024))) char obuf[2 * TQ::kBytes];
+  // stage s: its Q tile at 2 s kBytes, its dO tile right after it
+  __shared__ __attribute__((aligned(1024))) char qobuf[4 * TQ::kBytes];
   __shared__ __attribute__((aligned(16))) float rowbuf[2 * 2 * BQ];   // lse2 then D
 
   const int tid = threadIdx.x;
@@ -176,8 +176,9 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
       const int qc = min(rowq, Nq - 1);
       rowv = tid < BQ ? lseh[qc] : Dh[qc];
     }
-    copy_async<TQ, NW>(Qh, t * BQ, Nq, lds_addr(qbuf) + bufi * TQ::kBytes, wave, lofs);
-    copy_async<TQ, NW>(dOh, t * BQ, Nq, lds_addr(obuf) + bufi * TQ::kBytes, wave, lofs);
+    copy_async<TQ, NW>(Qh, t * BQ, Nq, lds_addr(qobuf) + bufi * 2 * TQ::kBytes, wave, lofs);
+    copy_async<TQ, NW>(dOh, t * BQ, Nq, lds_addr(qobuf) + (bufi * 2 + 1) * TQ::kBytes, wave,
+                       lofs);
   };
   auto finish_issue = [&](int bufi) FA_INLINE {
     __builtin_amdgcn_sched_barrier(0);
@@ -189,18 +190,42 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
     }
   };
 
+  // LDS addresses of this lane's operand reads.  qa[kk]: row read of k-step
+  // kk in the Q tile of the stage in use (the dO tile lies kBytes further);
+  // ta[db][h]: half h of the transposed read for output column block db, at
+  // k-step 0 of that Q tile (k-step ks2 lies 16 ks2 rows further); ka[kk]:
+  // row read of k-step kk in this wavefront's 32 K rows.  Each is the full
+  // swizzled address, formed once: when the stage flips, qa and ta move by
+  // 2 kBytes (3 NKK adds per tile in all), and every read is one address
+  // register plus a compile-time immediate.  xad() is opaque, so the
+  // compiler keeps these registers rather than redoing the lane arithmetic
+  // of each read.
   const OperandAddr<TQ> oa = operand_addr<TQ>(lane);
-  const char* kw_lds = kbuf + wave * 32 * RB;   // this wavefront's K rows
-  // row operand (contraction over d), k-step kk: rows r of `tile`
-  auto row_read = [&](const char* tile, int kk) FA_INLINE {
-    return as_bf16x8(*reinterpret_cast<const u32x4*>(tile + (oa.xr ^ (kk << 5)) + oa.ar));
+  int qa[NKK], ka[NKK], ta[NDB][2];
+  {
+    const int q0a = lds_addr(qobuf), k0a = lds_addr(kbuf) + wave * 32 * RB;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      qa[kk] = xad(oa.xr, kk << 5, oa.ar + q0a);
+      ka[kk] = xad(oa.xr, kk << 5, oa.ar + k0a);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      ta[db][0] = xad(oa.xt, db << 6, oa.at0 + q0a);
+      ta[db][1] = xad(oa.xt, db << 6, oa.at1 + q0a);
+    }
+  }
+  // row operand (contraction over d) of k-step kk at LDS address a[kk] + off
+  auto row_read = [&](const int (&a)[NKK], int kk, int off) FA_INLINE {
+    return as_bf16x8(lds_read_b128_at(a[kk], off));
   };
   // transposed operand (contraction over queries) for product j of a dV / dK
-  // step: k-step ks2 = j / NDB (queries 16 ks2 ..), output column block db
-  auto tr_read = [&](const char* tile, int j) FA_INLINE {
+  // step: k-step ks2 = j / NDB (queries 16 ks2 ..), output column block db;
+  // off = 0 for Q^T, kBytes for dO^T
+  auto tr_read = [&](int j, int off) FA_INLINE {
     const int ks2 = j / NDB, db = j % NDB;
-    const char* rk = tile + 16 * ks2 * RB + (oa.xt ^ (db << 6));
-    return bf16x8_from_halves(lds_tr_b64(rk + oa.at0), lds_tr_b64(rk + oa.at1));
+    const int o = off + 16 * ks2 * RB;
+    return bf16x8_from_halves(lds_tr_b64_at(ta[db][0], o), lds_tr_b64_at(ta[db][1], o));
   };
 
   // One query tile, in four steps of 2 NDB products each; LDS operands are
@@ -245,8 +270,6 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
 
   auto compute = [&](int stage, int t, int tn) FA_INLINE {
     constexpr int NJ = NKK;   // products per step (= 2 NDB)
-    const char* qt = qbuf + stage * TQ::kBytes;
-    const char* ot = obuf + stage * TQ::kBytes;
     const float* lse2 = rowbuf + stage * 2 * BQ;
     const float* dsum = lse2 + BQ;
     const int q0 = t * BQ;
@@ -260,16 +283,16 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < PF; ++j) {
-      fa[j] = row_read(qt, j);
-      fb[j] = row_read(kw_lds, j);
+      fa[j] = row_read(qa, j, 0);
+      fb[j] = row_read(ka, j, 0);
     }
     s = zero16();
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       s = mfma32x32x16(fa[j], fb[j], s);
       if (j + PF < NJ) {
-        fa[j + PF] = row_read(qt, j + PF);
-        fb[j + PF] = row_read(kw_lds, j + PF);
+        fa[j + PF] = row_read(qa, j + PF, 0);
+        fb[j + PF] = row_read(ka, j + PF, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -291,12 +314,12 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
     // 2. dP = dO V^T || P
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < PF; ++j) fa[j] = row_read(ot, j);
+    for (int j = 0; j < PF; ++j) fa[j] = row_read(qa, j, TQ::kBytes);
     dp = zero16();
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       dp = mfma32x32x16(fa[j], vf[j], dp);
-      if (j + PF < NJ) fa[j + PF] = row_read(ot, j + PF);
+      if (j + PF < NJ) fa[j + PF] = row_read(qa, j + PF, TQ::kBytes);
 #pragma unroll
       for (int i = j * 16 / NJ; i < (j + 1) * 16 / NJ; ++i) {
         // LSE (log2 units) of the four queries of registers (i/4)*4 .. +3
@@ -324,11 +347,11 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
     // same in step 2 or in dQ's mixed products measured slower or no change)
     __builtin_amdgcn_s_setprio(1);
 #pragma unroll
-    for (int j = 0; j < PF; ++j) fa[j] = tr_read(ot, j);
+    for (int j = 0; j < PF; ++j) fa[j] = tr_read(j, TQ::kBytes);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       dv[j % NDB] = mfma32x32x16(fa[j], pb[j / NDB], dv[j % NDB]);
-      if (j + PF < NJ) fa[j + PF] = tr_read(ot, j + PF);
+      if (j + PF < NJ) fa[j + PF] = tr_read(j + PF, TQ::kBytes);
 #pragma unroll
       for (int i = j * 16 / NJ; i < (j + 1) * 16 / NJ; ++i) {
         const float* dq4 = dsum + (i >> 2) * 8 + g * 4;
@@ -343,11 +366,11 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
     // 4. dK^T += Q^T dS
     __builtin_amdgcn_s_setprio(0);
 #pragma unroll
-    for (int j = 0; j < PF; ++j) fa[j] = tr_read(qt, j);
+    for (int j = 0; j < PF; ++j) fa[j] = tr_read(j, 0);
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       dk[j % NDB] = mfma32x32x16(fa[j], sb[j / NDB], dk[j % NDB]);
-      if (j + PF < NJ) fa[j + PF] = tr_read(qt, j + PF);
+      if (j + PF < NJ) fa[j + PF] = tr_read(j + PF, 0);
       if constexpr (DROPOUT) {
         // the next tile's two draws (unused after the last tile)
         if (j % (NJ / 2) == 0) draw_keep(tn * BQ, j / (NJ / 2));
@@ -382,6 +405,20 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
     if (DROPOUT || !(CAUSAL && t * BQ + BQ - 1 + dlt < kw)) compute(stage, t, tn);
     if (tn < nqt) finish_issue(stage ^ 1);
     t = tn;
+    // to the other stage's tiles
+    const int flip = stage ? -2 * TQ::kBytes : 2 * TQ::kBytes;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      qa[kk] += flip;
+      pin(qa[kk]);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      ta[db][0] += flip;
+      ta[db][1] += flip;
+      pin(ta[db][0]);
+      pin(ta[db][1]);
+    }
     stage ^= 1;
   }
 

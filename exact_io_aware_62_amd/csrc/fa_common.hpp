@@ -387,6 +387,22 @@ __device__ __forceinline__ u32x2 lds_tr_b64(const char* p) {
   const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
   return __builtin_bit_cast(u32x2, v);
 }
+// Reads at LDS byte address a + off, with off a compile-time constant that
+// goes into the instruction's offset field: the transpose read above, and a
+// plain 16-byte read.
+__device__ __forceinline__ u32x2 lds_tr_b64_at(int a, int off) {
+  typedef __attribute__((address_space(3))) char lds_char;
+  lds_char* p = reinterpret_cast<lds_char*>((size_t)(uint32_t)a) + off;
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)p);
+  return __builtin_bit_cast(u32x2, v);
+}
+__device__ __forceinline__ u32x4 lds_read_b128_at(int a, int off) {
+  typedef __attribute__((address_space(3))) char lds_char;
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  lds_char* p = reinterpret_cast<lds_char*>((size_t)(uint32_t)a) + off;
+  const u32x4 v = *reinterpret_cast<lds_u32x4*>(p);
+  return v;
+}
 
 // (a ^ b) + c in one v_xad_u32.  Written as asm so that loop-invariant
 // address arithmetic is recomputed where it is used instead of being hoisted
