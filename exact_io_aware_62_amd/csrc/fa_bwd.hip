@@ -472,9 +472,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   using T = LdsTile<BK, D>;
   constexpr int RB = T::kRowBytes;
   // two stages of the K and V tiles, filled by copy_async; the stage is
-  // chosen at run time so one loop body serves both
-  __shared__ __attribute__((aligned(1024))) char kbuf[2 * T::kBytes];
-  __shared__ __attribute__((aligned(1024))) char vbuf[2 * T::kBytes];
+  // chosen at run time so one loop body serves both.  Stage s: its K tile at
+  // 2 s kBytes, its V tile right after it.
+  __shared__ __attribute__((aligned(1024))) char kvbuf[4 * T::kBytes];
+  constexpr int KB = T::kBytes;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
@@ -557,31 +558,46 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
 
   const auto lofs = T::template lane_offsets<NW>(wave, lane);
   auto issue = [&](int t, int stage) FA_INLINE {
-    copy_async<T, NW>(Kh, t * BK, Nk, lds_addr(kbuf) + stage * T::kBytes, wave, lofs);
-    copy_async<T, NW>(Vh, t * BK, Nk, lds_addr(vbuf) + stage * T::kBytes, wave, lofs);
+    copy_async<T, NW>(Kh, t * BK, Nk, lds_addr(kvbuf) + 2 * stage * KB, wave, lofs);
+    copy_async<T, NW>(Vh, t * BK, Nk, lds_addr(kvbuf) + (2 * stage + 1) * KB, wave, lofs);
   };
 
   constexpr int NS = 4 * NKK + 4 * NDB;   // products per tile
   constexpr int PF = 3;                   // operand reads issued this many products ahead
+  // LDS addresses of this lane's operand reads in the K tile of the stage in
+  // use (the V tile lies kBytes further): ra[kk], row read of k-step kk in
+  // key rows 0..31 (rows 32..63 lie 32 rows further); ta[db][h], half h of
+  // the transposed read for output column block db at keys 0..15.  Each is
+  // the full swizzled address, formed once (xad() is opaque, so the compiler
+  // keeps these registers rather than redoing the lane arithmetic of each
+  // read); when the stage flips they move by 2 kBytes, and every read is
+  // one address register plus a compile-time immediate.
+  int ra[NKK], ta[NDB][2];
+  {
+    const int a0 = lds_addr(kvbuf);
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) ra[kk] = xad(oa.xr, kk << 5, oa.ar + a0);
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      ta[db][0] = xad(oa.xt, db << 6, oa.at0 + a0);
+      ta[db][1] = xad(oa.xt, db << 6, oa.at1 + a0);
+    }
+  }
   // operand of product j (see the schedule above)
-  auto operand = [&](const char* kt, const char* vt, int j) FA_INLINE -> bf16x8 {
+  auto operand = [&](int j) FA_INLINE -> bf16x8 {
     if (j < 4 * NKK) {
-      const char* base = j < 2 * NKK ? kt : vt;
       const int kb = (j / NKK) & 1, kk = j % NKK;
-      return as_bf16x8(*reinterpret_cast<const u32x4*>(base + kb * 32 * RB + (oa.xr ^ (kk << 5)) +
-                                                         oa.ar));
+      return as_bf16x8(lds_read_b128_at(ra[kk], (j < 2 * NKK ? 0 : KB) + kb * 32 * RB));
     }
     const int jj = j - 4 * NKK, kb = jj / (2 * NDB), ks2 = (jj / NDB) & 1, db = jj % NDB;
-    const char* rk = kt + (kb * 32 + 16 * ks2) * RB + (oa.xt ^ (db << 6));
-    return bf16x8_from_halves(lds_tr_b64(rk + oa.at0), lds_tr_b64(rk + oa.at1));
+    const int o = (kb * 32 + 16 * ks2) * RB;
+    return bf16x8_from_halves(lds_tr_b64_at(ta[db][0], o), lds_tr_b64_at(ta[db][1], o));
   };
 
   // D as the loop uses it: times 1 - p with dropout (see the kernel comment);
   // set once D is known, after the rows are read below
   float dsum_k = 0.f;
-  auto compute = [&](int stage, int t) FA_INLINE {
-    const char* kt = kbuf + stage * T::kBytes;
-    const char* vt = vbuf + stage * T::kBytes;
+  auto compute = [&](int t) FA_INLINE {
     const int k0 = t * BK;
     const bool need_mask = (CAUSAL && k0 + BK - 1 > q0w + dlt) || (k0 + BK > Nk);
     f32x16 s[2], dp[2];
@@ -593,7 +609,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     bf16x8 fr[NS];
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < PF; ++j) fr[j] = operand(kt, vt, j);
+    for (int j = 0; j < PF; ++j) fr[j] = operand(j);
     static_for<0, NS>([&](auto jc) FA_INLINE {
       constexpr int j = decltype(jc)::value;
       if constexpr (j < 2 * NKK) {
@@ -606,7 +622,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
         constexpr int jj = j - 4 * NKK, kb = jj / (2 * NDB), ks2 = (jj / NDB) & 1, db = jj % NDB;
         dq[db] = mfma32x32x16(fr[j], ds[kb * 2 + ks2], dq[db]);
       }
-      if constexpr (j + PF < NS) fr[j + PF] = operand(kt, vt, j + PF);
+      if constexpr (j + PF < NS) fr[j + PF] = operand(j + PF);
       if constexpr (DROPOUT && j < 2 * NKK && j % (2 * NKK / 4) == 0) {
         // four draws per tile, spread over the S^T products.  One draw decides
         // four keys of this lane's row and of lane r ^ 1's (rows 2 ig, 2 ig + 1:
@@ -697,21 +713,21 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
       f[kk] = as_bf16x8(qrow < Nq ? *reinterpret_cast<const u32x4*>(rows + (oa.xr ^ (kk << 5)) + oa.ar)
                                   : zero_u32x4());
   };
-  copy_block(p.dO + qhead, lds_addr(kbuf), lds_addr(kbuf) + T::kBytes);
-  if constexpr (FUSED_D) copy_block(p.O + qhead, lds_addr(vbuf), lds_addr(vbuf) + T::kBytes);
+  copy_block(p.dO + qhead, lds_addr(kvbuf), lds_addr(kvbuf) + 2 * KB);
+  if constexpr (FUSED_D) copy_block(p.O + qhead, lds_addr(kvbuf) + KB, lds_addr(kvbuf) + 3 * KB);
   wait_vmem();
   __syncthreads();
-  read_rows(kbuf + (wave >> 1) * T::kBytes + wrow, of);
-  form_d(vbuf + (wave >> 1) * T::kBytes + wrow);
+  read_rows(kvbuf + (wave >> 1) * 2 * KB + wrow, of);
+  form_d(kvbuf + ((wave >> 1) * 2 + 1) * KB + wrow);
   dsum_k = DROPOUT ? dsum * p.drop_keep : dsum;
   if (t_first < ntiles) {
     __syncthreads();   // every wavefront has read its dO and O rows
-    copy_async<T, NW>(p.Q + qhead, r0, Nq, lds_addr(kbuf) + T::kBytes, wave, lofs);
-    if (upper) copy_async<T, NW>(p.Q + qhead, r0 + 64, Nq, lds_addr(vbuf) + T::kBytes, wave, lofs);
+    copy_async<T, NW>(p.Q + qhead, r0, Nq, lds_addr(kvbuf) + 2 * KB, wave, lofs);
+    if (upper) copy_async<T, NW>(p.Q + qhead, r0 + 64, Nq, lds_addr(kvbuf) + 3 * KB, wave, lofs);
     issue(t_first, 0);
     wait_vmem();
     __syncthreads();
-    read_rows((wave < 2 ? kbuf : vbuf) + T::kBytes + wrow, qf);
+    read_rows(kvbuf + (wave < 2 ? 2 : 3) * KB + wrow, qf);
   }
   int t = t_first;
   int stage = 0;
@@ -722,8 +738,22 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     const int tn = next_tile(t + 1);
     if (tn < ntiles) issue(tn, stage ^ 1);
     // a tile entirely above this wavefront's causal diagonal contributes 0
-    if (!(CAUSAL && t * BK > q0w + 31 + dlt)) compute(stage, t);
+    if (!(CAUSAL && t * BK > q0w + 31 + dlt)) compute(t);
     t = tn;
+    // to the other stage's tiles
+    const int flip = stage ? -2 * KB : 2 * KB;
+#pragma unroll
+    for (int kk = 0; kk < NKK; ++kk) {
+      ra[kk] += flip;
+      pin(ra[kk]);
+    }
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      ta[db][0] += flip;
+      ta[db][1] += flip;
+      pin(ta[db][0]);
+      pin(ta[db][1]);
+    }
     stage ^= 1;
   }
 
@@ -736,7 +766,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
     // with no key tile there was no loop barrier after the dO and O reads
     if (t_first >= ntiles) __syncthreads();
     if (q0w < Nq) {
-      char* st = (wave < 2 ? kbuf : vbuf) + stage * T::kBytes + (wave & 1) * 32 * RB;
+      char* st = kvbuf + (2 * stage + (wave < 2 ? 0 : 1)) * KB + (wave & 1) * 32 * RB;
       store_rows_staged<D>(st, dq, DROPOUT ? p.scale * p.drop_scale : p.scale,
                            p.dQ + qhead + (size_t)q0w * D, Nq - q0w, lane);
     }
