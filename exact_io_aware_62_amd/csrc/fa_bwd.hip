@@ -98,7 +98,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char kbuf[TK::kBytes];
   // stage s: its Q tile at 2 s kBytes, its dO tile right after it
   __shared__ __attribute__((aligned(1024))) char qobuf[4 * TQ::kBytes];
-  __shared__ __attribute__((aligned(16))) float rowbuf[2 * 2 * BQ];   // lse2 then D
+  __shared__ __attribute__((aligned(16))) float rowbuf[2 * 2 * BQ];   // lse2, then D (-D without dropout)
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, r = lane & 31, g = lane >> 5;
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
     if (tid < 2 * BQ) {
       float v;
       if (tid < BQ) v = rowq < Nq ? lse_to_log2(rowv) : INFINITY;
-      else v = rowq < Nq ? (DROPOUT ? rowv * p.drop_keep : rowv) : 0.f;
+      else v = rowq < Nq ? (DROPOUT ? rowv * p.drop_keep : -rowv) : 0.f;
       rowbuf[bufi * 2 * BQ + tid] = v;
     }
   };
@@ -315,7 +315,18 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < PF; ++j) fa[j] = row_read(qa, j, TQ::kBytes);
-    dp = zero16();
+    if constexpr (DROPOUT) {
+      dp = zero16();
+    } else {
+      // the dP accumulator starts at -D of each register's query, so the
+      // products leave dP - D (this form's row buffer holds -D)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(dsum + k * 8 + g * 4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dp[4 * k + e] = __uint_as_float(v[e]);
+      }
+    }
 #pragma unroll
     for (int j = 0; j < NJ; ++j) {
       dp = mfma32x32x16(fa[j], vf[j], dp);
@@ -354,10 +365,13 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
       if (j + PF < NJ) fa[j + PF] = tr_read(j + PF, TQ::kBytes);
 #pragma unroll
       for (int i = j * 16 / NJ; i < (j + 1) * 16 / NJ; ++i) {
-        const float* dq4 = dsum + (i >> 2) * 8 + g * 4;
-        float dpv = dp[i];
-        if constexpr (DROPOUT) dpv = ((keepbits >> i) & 1u) ? dpv : 0.f;
-        dp[i] = s[i] * (dpv - dq4[i & 3]);
+        if constexpr (DROPOUT) {
+          const float* dq4 = dsum + (i >> 2) * 8 + g * 4;
+          const float dpv = ((keepbits >> i) & 1u) ? dp[i] : 0.f;
+          dp[i] = s[i] * (dpv - dq4[i & 3]);
+        } else {
+          dp[i] = s[i] * dp[i];
+        }
         if ((i & 7) == 7) sb[i >> 3] = pack_c8(dp, i - 7);
       }
       __builtin_amdgcn_sched_barrier(0);
@@ -597,6 +611,13 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   // D as the loop uses it: times 1 - p with dropout (see the kernel comment);
   // set once D is known, after the rows are read below
   float dsum_k = 0.f;
+  // At d = 128 without dropout the dP^T products of each key block start
+  // from -D (this register block, the same value in all 16 entries) instead
+  // of 0, so they leave dP - D.  At d = 64 the 16 extra registers would cost
+  // a wavefront per SIMD, and with dropout dropped entries need D alone; those
+  // forms start from 0 and subtract D.
+  constexpr bool kFoldD = !DROPOUT && D == 128;
+  f32x16 negd = zero16();
   auto compute = [&](int t) FA_INLINE {
     const int k0 = t * BK;
     const bool need_mask = (CAUSAL && k0 + BK - 1 > q0w + dlt) || (k0 + BK > Nk);
@@ -617,7 +638,7 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
         s[kb] = mfma32x32x16(fr[j], qf[kk], s[kb]);
       } else if constexpr (j < 4 * NKK) {
         constexpr int kb = (j - 2 * NKK) / NKK, kk = j % NKK;
-        dp[kb] = mfma32x32x16(fr[j], of[kk], dp[kb]);
+        dp[kb] = mfma32x32x16(fr[j], of[kk], kk == 0 ? negd : dp[kb]);
       } else {
         constexpr int jj = j - 4 * NKK, kb = jj / (2 * NDB), ks2 = (jj / NDB) & 1, db = jj % NDB;
         dq[db] = mfma32x32x16(fr[j], ds[kb * 2 + ks2], dq[db]);
@@ -672,10 +693,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
               pin(pv);
               s[kb][i] = pv;
             } else {
-              float dpv = dp[kb][i];
+              float dpv = dp[kb][i];   // dP - D if kFoldD, else dP
               if constexpr (DROPOUT)
                 dpv = ((keepbits >> (kb * 16 + i)) & 1u) ? dpv : 0.f;
-              float dsv = s[kb][i] * (dpv - dsum_k);
+              float dsv = kFoldD ? s[kb][i] * dpv : s[kb][i] * (dpv - dsum_k);
               pin(dsv);
               dp[kb][i] = dsv;
               if constexpr ((i & 7) == 7) {
@@ -720,6 +741,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
   read_rows(kvbuf + (wave >> 1) * 2 * KB + wrow, of);
   form_d(kvbuf + ((wave >> 1) * 2 + 1) * KB + wrow);
   dsum_k = DROPOUT ? dsum * p.drop_keep : dsum;
+  if constexpr (kFoldD) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) negd[i] = -dsum;
+  }
   if (t_first < ntiles) {
     __syncthreads();   // every wavefront has read its dO and O rows
     copy_async<T, NW>(p.Q + qhead, r0, Nq, lds_addr(kvbuf) + 2 * KB, wave, lofs);
