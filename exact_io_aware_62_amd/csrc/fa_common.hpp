@@ -156,6 +156,21 @@ struct DropoutStream {
   }
 };
 
+// The keep rule on a packed pair: for each 16-bit half h of a Philox output
+// word w, 0xFFFF if h >= thresh (kept) and 0 otherwise (thresh = 0 keeps
+// everything).  Three packed 16-bit instructions: the saturating difference
+// thresh - h (0 exactly when kept), its minimum with 1, and that minus 1.
+// ANDed with a packed bf16 pair it zeroes the dropped entries.  tt holds
+// thresh in both halves, ones 0x00010001.  Written as asm: the compiler turns
+// the same expression into two compares, two selects and a byte permute.
+__device__ __forceinline__ uint32_t drop_mask(uint32_t w, uint32_t tt, uint32_t ones) {
+  uint32_t d, m, r;
+  asm("v_pk_sub_u16 %0, %1, %2 clamp" : "=v"(d) : "s"(tt), "v"(w));
+  asm("v_pk_min_u16 %0, %1, %2" : "=v"(m) : "v"(d), "s"(ones));
+  asm("v_pk_sub_u16 %0, %1, %2" : "=v"(r) : "v"(m), "s"(ones));
+  return r;
+}
+
 // Value of lane l ^ 1 (DPP quad permute 1, 0, 3, 2).
 __device__ __forceinline__ uint32_t pair_swap(uint32_t x) {
   return (uint32_t)__builtin_amdgcn_mov_dpp((int)x, 1 | (0 << 2) | (3 << 4) | (2 << 6), 0xF, 0xF,

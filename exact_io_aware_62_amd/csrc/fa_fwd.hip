@@ -56,8 +56,10 @@ namespace fa {
 // ranges of p.tiles_per_split tiles, one workgroup each; a workgroup writes
 // its normalised partial O (fp32) and partial LSE to p.Opart / p.LSEpart, and
 // combine_kernel merges the ranges with the log-sum-exp rule.
+// Two wavefronts per SIMD at d = 128, three at d = 64 (168 registers: left to
+// itself the compiler lets the sparse dropout form grow just past that).
 template <int D, bool CAUSAL, bool SPARSE, int MODE>
-__global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(D == 64 ? 3 : 2))) void fwd_kernel(FwdParams p) {
   constexpr bool DROPOUT = MODE == 1, SPLIT = MODE == 2;
   constexpr int BQ = 128, BK = 64, NW = 4;
   constexpr float kSlack = 8.0f;
@@ -125,8 +127,6 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
   float m_run = kNegBig;   // running max of scaled scores (log2 domain)
   float l_run = 0.f;       // running partial row sum (this lane's keys)
   const float c = p.scale_log2;
-  // keep bits of the current tile: bit kb*16 + i for register i of key block kb
-  uint32_t keepbits = 0xFFFFFFFFu;
   DropoutStream ds_;
   if constexpr (DROPOUT) {
     ds_.seed_lo = p.seed_lo;
@@ -135,35 +135,48 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
     ds_.offset = p.drop_offset;
     ds_.thresh = p.drop_thresh;
   }
-  // One draw decides four keys of this lane's row and of the row of lane
-  // r ^ 1 (rows 2 ig, 2 ig + 1: q0w is even).  Key group u = kb*4 + m (keys
-  // k0 + kb*32 + m*8 + g*4 + 0..3, keep bits 4u .. 4u+3) is drawn by the lane
-  // of the pair whose row parity equals u's: draw v of a tile takes group
-  // u = 2v + (r & 1).  The bits for the other row are handed over with one
-  // lane swap once the tile's four draws are made.  The previous tile's bits
-  // are dead by then (its P was packed in the previous iteration), so this
-  // lane's own bits collect in keepbits directly.
-  uint32_t keep_give = 0;
+  // Dropout: one draw decides four keys of this lane's row and of the row of
+  // lane r ^ 1 (rows 2 ig, 2 ig + 1: q0w is even).  Key group u = kb*4 + m
+  // (keys k0 + kb*32 + m*8 + g*4 + 0..3) is drawn by the lane of the pair
+  // whose row parity equals u's: draw v of a tile takes group u = 2v + (r & 1),
+  // and each lane hands the other row's two words to its partner.  kx[2u + h]
+  // holds drop_mask() for keys 2h, 2h + 1 of group u in this lane's row,
+  // which is word q = 2(u % 2) + h of P's packed B operand pb[u / 2].  The
+  // previous tile's entries are dead by then (its P was packed in the
+  // previous iteration), so the draws write kx in place.
+  uint32_t kx[DROPOUT ? 16 : 1];
   auto draw_keep = [&](int tc, int v) FA_INLINE {
     const int odd = qrow & 1;
     const int u = 2 * v + odd, kb = u >> 2, m = u & 3;
-    const uint32_t bits =
-        ds_.keep8((uint32_t)(tc * (BK / 4) + kb * 8 + m * 2 + g), (uint32_t)qrow >> 1);
-    const uint32_t own = ((odd ? bits >> 4 : bits) & 0xFu) << (4 * u);
-    const uint32_t give = ((odd ? bits : bits >> 4) & 0xFu) << (4 * u);
-    keepbits = v == 0 ? own : keepbits | own;
-    keep_give = v == 0 ? give : keep_give | give;
-    pin(keepbits);
-    pin(keep_give);
+    const u32x4 w = philox4x32_10((uint32_t)(tc * (BK / 4) + kb * 8 + m * 2 + g),
+                                  (uint32_t)qrow >> 1, ds_.bh, ds_.offset, ds_.seed_lo,
+                                  ds_.seed_hi);
+    // words 0, 1: the block's even row; words 2, 3: its odd row
+    const uint32_t tt = ds_.thresh * 0x10001u;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t ev = drop_mask(w[h], tt, 0x10001u), od = drop_mask(w[2 + h], tt, 0x10001u);
+      // both lanes of the pair swap both words (a swap under a lane-dependent
+      // condition would read a lane that is switched off); then group 2v takes
+      // the even lane's draw and group 2v + 1 the odd lane's
+      const uint32_t sev = pair_swap(ev), sod = pair_swap(od);
+      kx[4 * v + h] = odd ? sod : ev;
+      kx[4 * v + 2 + h] = odd ? od : sev;
+      pin(kx[4 * v + h]);
+      pin(kx[4 * v + 2 + h]);
+    }
   };
-  auto finish_keep = [&]() FA_INLINE {
-    keepbits |= pair_swap(keep_give);
-    pin(keepbits);
-  };
-  // P as it enters the P V product: kept, or 0 (1 / (1 - p) comes at the end)
-  auto dropped = [&](float pe, int e) FA_INLINE -> float {
-    if constexpr (DROPOUT) return ((keepbits >> e) & 1u) ? pe : 0.f;
-    return pe;
+  // P's packed B operand entry q with the dropped probabilities zeroed (1 / (1 - p)
+  // comes at the end)
+  auto pack_p = [&](const f32x16& s, int base, int q) FA_INLINE -> bf16x8 {
+    bf16x8 r = pack_c8(s, base);
+    if constexpr (DROPOUT) {
+      u32x4 wv = __builtin_bit_cast(u32x4, r);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wv[i] &= kx[4 * q + i];
+      r = __builtin_bit_cast(bf16x8, wv);
+    }
+    return r;
   };
 
   const auto lofs = T::template lane_offsets<NW>(wave, lane);
@@ -182,13 +195,9 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) s[kb][i] = exp2_fast(__builtin_fmaf(s[kb][i], c, -m_run));
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      f32x16 t = s[kb];
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) t[i] = dropped(s[kb][i], kb * 16 + i);
-#pragma unroll
-      for (int ks2 = 0; ks2 < 2; ++ks2) pb[kb * 2 + ks2] = pack_c8(t, 8 * ks2);
-    }
+      for (int ks2 = 0; ks2 < 2; ++ks2) pb[kb * 2 + ks2] = pack_p(s[kb], 8 * ks2, kb * 2 + ks2);
   };
   auto rowsum = [&](const f32x16 (&s)[2]) {
     float a0 = 0.f, a1 = 0.f, a2 = 0.f, a3 = 0.f;
@@ -331,7 +340,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       for (int e = e0; e < e1; ++e) {
         const int b = e >> 4, i = e & 15;
         const float pe = pes[e - e0];
-        sc[b][i] = dropped(pe, e);
+        sc[b][i] = pe;
         // the row sum is taken over the fp32 probabilities: a sum of the
         // bf16-rounded ones would move LSE by up to 2^-9 on short rows
         if (e & 1) {
@@ -342,7 +351,7 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
           pin(a0);
         }
         if ((i & 7) == 7) {
-          pb[b * 2 + (i >> 3)] = pack_c8(sc[b], i - 7);
+          pb[b * 2 + (i >> 3)] = pack_p(sc[b], i - 7, b * 2 + (i >> 3));
           pin(pb[b * 2 + (i >> 3)]);
         }
       }
@@ -389,7 +398,6 @@ __global__ __launch_bounds__(256, 2) void fwd_kernel(FwdParams p) {
       if constexpr (DROPOUT) {
         // four draws per tile, spread over the score products
         if (j % (NJ / 4) == 0) draw_keep(tc, j / (NJ / 4));
-        if (j == NJ - 1) finish_keep();
       }
       __builtin_amdgcn_sched_barrier(0);
     }
