@@ -713,9 +713,10 @@ __global__ __launch_bounds__(256, 2) void dq_kernel(BwdParams p) {
 
   // The rows of the workgroup's query block arrive as whole-row copies into
   // LDS (a lane loading its own row would touch 32 rows per load), in two
-  // phases that each fill both stages of the two tile buffers:
-  //   1. dO -> K buffers, O -> V buffers; read of[] and form D;
-  //   2. Q -> stage 1 of both buffers while the first key tile goes to
+  // phases that each fill all four tile slots of kvbuf:
+  //   1. dO -> the K tiles of both stages, O -> the V tiles; read of[] and
+  //      form D;
+  //   2. Q -> the K and V tiles of stage 1 while the first key tile goes to
   //      stage 0; read qf[].  The first iteration's barrier orders these
   //      reads before the copy that refills stage 1.
   // Rows 32 w .. 32 w + 31 of the block sit in stage w / 2, rows
