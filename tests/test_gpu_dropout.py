@@ -183,3 +183,33 @@ def test_dropout_zero_is_the_plain_path(fa):
     torch.cuda.synchronize()
     assert torch.equal(o0, o1) and torch.equal(l0, l1)
     assert all(torch.equal(x, y) for x, y in zip(g0, g1))
+
+
+@pytest.mark.parametrize("d,N,causal", [(128, 256, True), (128, 256, False), (64, 192, True),
+                                        (64, 192, False)])
+def test_forward_zeroes_exactly_the_dropped_entries(fa, d, N, causal):
+    """Element-by-element check of the keep rule as the forward applies it.
+
+    With V rows s..s+d-1 set to the unit vectors and every other row 0,
+    O[i, c] = keep(i, s + c) P(i, s + c) / (l_i (1 - p)), which is nonzero
+    exactly when key s + c is visible to query i and kept: the zero pattern
+    of O is the keep mask of those d keys, with no tolerance involved.
+    """
+    torch = torch_mod()
+    B, H, p, seed, offset = 1, 2, 0.3, 77, 3
+    bits = synth.draw_inputs(B, H, N, d, 11)
+    q, k = to_gpu(bits["q"]), to_gpu(bits["k"])
+    allowed = oracle.allowed_mask(N, N, causal, None, 128)
+    for s in range(0, N, d):
+        v = torch.zeros((B, H, N, d), dtype=torch.bfloat16, device=q.device)
+        v[:, :, s:s + d, :] = torch.eye(d, dtype=torch.bfloat16, device=q.device)
+        o, _ = fa.forward(q, k, v, 1.0 / d ** 0.5, causal, None, 128, dropout_p=p, seed=seed,
+                          offset=offset)
+        torch.cuda.synchronize()
+        nz = (o.float() != 0).cpu().numpy()
+        for bh in range(B * H):
+            b, h = divmod(bh, H)
+            keep = oracle.keep_mask(N, N, bh, p, seed, offset)
+            want = (allowed & keep)[:, s:s + d]
+            bad = np.argwhere(nz[b, h] != want)
+            assert bad.size == 0, (s, bh, bad[:5].tolist())
