@@ -367,8 +367,8 @@ def main():
         log("[bench] copy calibration: 3 copies of 1 GiB done")
         return
     if args.gpus != 1:
-        log(f"bench.py: this build runs on exactly one GPU; --gpus {args.gpus} is not "
-            "supported (heads shard across GPUs with no exchange; see the design notes).")
+        log(f"bench.py times one GPU; --gpus {args.gpus} is not supported (the heads "
+            "would shard across GPUs with no exchange between them).")
         sys.exit(2)
 
     import torch
