@@ -149,7 +149,7 @@ def sample_clock(run, seconds: float, torch, dev):
 def gemm_reference(torch, dev, n: int = 8192, reps: int = 10):
     """TFLOP/s of a plain dense bf16 product (n x n x n, torch.matmul -> hipBLASLt) on the
     same GPU, median of `reps` timed calls: what a matrix-core-bound library kernel
-    reaches on this machine at the clock it runs at, as context for the attention kernels'
+    reaches on this GPU at the clock it runs at, as context for the attention kernels'
     own rates (the roofline's peak stays the published one)."""
     a = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
     b = torch.randn(n, n, device=dev, dtype=torch.bfloat16)
