@@ -196,7 +196,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
   // k-step 0 of that Q tile (k-step ks2 lies 16 ks2 rows further); ka[kk]:
   // row read of k-step kk in this wavefront's 32 K rows.  Each is the full
   // swizzled address, formed once: when the stage flips, qa and ta move by
-  // 2 kBytes (3 NKK adds per tile in all), and every read is one address
+  // 2 kBytes (2 NKK adds per tile in all), and every read is one address
   // register plus a compile-time immediate.  xad() is opaque, so the
   // compiler keeps these registers rather than redoing the lane arithmetic
   // of each read.
