@@ -312,6 +312,7 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
     }
 
     // 2. dP = dO V^T || P
+    u32x4 l4;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int j = 0; j < PF; ++j) fa[j] = row_read(qa, j, TQ::kBytes);
@@ -333,9 +334,10 @@ __global__ __launch_bounds__(256, 2) void dkdv_kernel(BwdParams p) {
       if (j + PF < NJ) fa[j + PF] = row_read(qa, j + PF, TQ::kBytes);
 #pragma unroll
       for (int i = j * 16 / NJ; i < (j + 1) * 16 / NJ; ++i) {
-        // LSE (log2 units) of the four queries of registers (i/4)*4 .. +3
-        const float* lq = lse2 + (i >> 2) * 8 + g * 4;
-        s[i] = exp2_fast(__builtin_fmaf(s[i], c, -lq[i & 3]));
+        // LSE (log2 units) of the four queries of registers (i/4)*4 .. +3,
+        // one 16-byte read per four registers
+        if ((i & 3) == 0) l4 = *reinterpret_cast<const u32x4*>(lse2 + (i >> 2) * 8 + g * 4);
+        s[i] = exp2_fast(__builtin_fmaf(s[i], c, -__uint_as_float(l4[i & 3])));
         if ((i & 7) == 7) {
           if constexpr (DROPOUT) {
             // dV takes the kept, rescaled probabilities; dS below takes P
